@@ -1,0 +1,328 @@
+"""Benchmark of the expert-ID matmul path on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic
+input: router (sigmoid + selection bias, top-k) -> expert-ID matmul ->
+gate-weighted combine, all in the library's HIP kernels.
+
+Headline (`value`): decode, m=1, k=4096, n=1536, top-8 of 256 bf16 experts,
+as effective GB/s of touched expert weights (8 x 1536 x 4096 x 2 B per step)
+over the whole step.  Decode is timed cold: step i routes with the experts
+relabelled so that its picks are experts 8i..8i+7, so 32 consecutive steps
+sweep all 3.2 GB of weights and none is served from the 256 MB Infinity
+Cache.  The prefill configurations (m=2048 down projection with per-slot
+input; m=512 balanced and maximally skewed) are reported next to it in
+TFLOP/s.
+
+Steps are captured once into a HIP graph and replayed (the CPU cost of
+launching would otherwise exceed a decode step); per-kernel durations come
+from HIP events around each matmul call in an eager pass of the same steps,
+recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from expert_id_matmul_amd import binding as B  # noqa: E402
+from expert_id_matmul_amd import workloads as W  # noqa: E402
+
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+F32_PEAK = 157.3e12          # flop/s, MI355X dense f32 matrix
+ROT = 32                     # decode steps per full sweep of the experts
+
+
+def _dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _percentiles(v):
+    v = sorted(v)
+    n = len(v)
+    return {"p25": v[(n - 1) // 4], "median": v[n // 2], "p75": v[3 * (n - 1) // 4]}
+
+
+def _relabel(n_experts: int, picks: np.ndarray, target: np.ndarray) -> np.ndarray:
+    """A permutation p of experts with p[picks[j]] = target[j]; every other
+    expert keeps its order among the remaining labels."""
+    p = np.full(n_experts, -1, dtype=np.int64)
+    p[picks] = target
+    rest_src = [e for e in range(n_experts) if p[e] < 0]
+    used = set(int(t) for t in target)
+    rest_dst = [e for e in range(n_experts) if e not in used]
+    p[rest_src] = rest_dst
+    return p
+
+
+class Timed:
+    """Capture `steps` calls of step_fn into a graph, replay it, and time it."""
+
+    def __init__(self, step_fn, steps_per_graph: int):
+        self.step_fn = step_fn
+        self.n = steps_per_graph
+        self.graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(self.n):  # eager warm-up on the capture stream
+                step_fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph):
+            for i in range(self.n):
+                step_fn(i)
+        torch.cuda.synchronize()
+
+    def run(self, steps: int, warmup: int):
+        reps = max(1, -(-steps // self.n))
+        wreps = max(1, -(-warmup // self.n)) if warmup > 0 else 0
+        for _ in range(wreps):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            self.graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        done = reps * self.n
+        return {"steps": done, "gpu_ms_per_step": start.elapsed_time(end) / done,
+                "wall_ms_per_step": wall * 1e3 / done}
+
+
+def kernel_times(call, steps: int):
+    """HIP events around `call(i)` for i < steps (eager, same stream)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        call(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+# ---------------------------------------------------------------------- decode
+def bench_decode(lib, steps: int, warmup: int):
+    wl = W.WORKLOADS["decode"]
+    shape = B.shape_of(wl)
+    weights = torch.empty(wl.weight_bytes, dtype=torch.uint8, device="cuda")
+    W.fill_weights(wl, weights)
+    x = _dev(W.activations(wl))
+    logits0 = W.router_logits(wl)[0]
+    bias0 = W.router_bias(wl)
+    # the picks of the unrelabelled router, from the library's own router
+    ids0 = torch.empty((1, wl.top_k), dtype=torch.int32, device="cuda")
+    lib.route_topk(_dev(logits0[None]), _dev(bias0), wl.top_k, ids0, None)
+    picks = ids0.cpu().numpy().view(np.uint32)[0].astype(np.int64)
+    logits = np.empty((ROT, wl.n_experts), np.float32)
+    bias = np.empty((ROT, wl.n_experts), np.float32)
+    for i in range(ROT):
+        p = _relabel(wl.n_experts, picks, np.arange(wl.top_k) + wl.top_k * i)
+        logits[i, p] = logits0
+        bias[i, p] = bias0
+    logits_d, bias_d = _dev(logits), _dev(bias)
+    ids = torch.empty((wl.m, wl.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((wl.m, wl.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.m, wl.n), dtype=torch.float32, device="cuda")
+
+    def route(i):
+        lib.route_topk(logits_d[i % ROT][None], bias_d[i % ROT], wl.top_k, ids, gates)
+
+    def matmul(i):
+        lib.matmul_id(shape, B.DIRECT, weights, x, ids, y, weight_bytes=wl.weight_bytes)
+
+    def combine(i):
+        lib.combine(y, gates, out)
+
+    def step(i):
+        route(i)
+        matmul(i)
+        combine(i)
+
+    timed = Timed(step, ROT)
+    res = timed.run(steps, warmup)
+    # the graph's last step against the same step run eagerly
+    graph_out = out.clone()
+    graph_ids = ids.clone()
+    step(ROT - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(graph_out, out) and torch.equal(graph_ids, ids), "graph replay differs from eager"
+    assert sorted(graph_ids.cpu().numpy()[0].tolist()) == list(range(8 * (ROT - 1), 8 * ROT))
+    # per-kernel: the Direct kernel alone, eager, between the same route/combine launches
+    direct_ms = []
+    for rep in range(max(1, steps // ROT)):
+        for i in range(ROT):
+            route(i)
+            direct_ms += kernel_times(lambda _: matmul(i), 1)
+            combine(i)
+    touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
+    med = _percentiles(direct_ms)["median"]
+    avg = float(np.mean(direct_ms))
+    res.update({
+        "touched_bytes": touched,
+        "value_gbs": touched / (res["gpu_ms_per_step"] * 1e-3) / 1e9,
+        "direct_ms": {"avg": avg, **_percentiles(direct_ms), "n": len(direct_ms)},
+        "direct_gbs": touched / (avg * 1e-3) / 1e9,
+        "direct_gbs_median": touched / (med * 1e-3) / 1e9,
+    })
+    del weights
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------- prefill
+def bench_prefill(lib, name: str, steps: int, warmup: int):
+    wl = W.WORKLOADS[name]
+    shape = B.shape_of(wl)
+    weights = torch.empty(wl.weight_bytes, dtype=torch.uint8, device="cuda")
+    W.fill_weights(wl, weights)
+    x = _dev(W.activations(wl))
+    ids = torch.empty((wl.m, wl.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((wl.m, wl.top_k), dtype=torch.float32, device="cuda")
+    routed = wl.ids_kind == "logits"
+    if routed:
+        logits = _dev(W.router_logits(wl))
+        bias = _dev(W.router_bias(wl))
+    else:
+        ids.copy_(_dev(W.ids(wl).view(np.int32)))
+        gates.copy_(_dev(W.gates(wl)))
+    y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
+    out = torch.empty((wl.m, wl.n), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(lib.query(shape, B.GROUPED).scratch_bytes, dtype=torch.uint8, device="cuda")
+
+    def matmul(i, route=B.GROUPED):
+        lib.matmul_id(shape, route, weights, x, ids, y, scratch, weight_bytes=wl.weight_bytes)
+
+    def step(i):
+        if routed:
+            lib.route_topk(logits, bias, wl.top_k, ids, gates)
+        matmul(i)
+        lib.combine(y, gates, out)
+
+    timed = Timed(step, 4)
+    res = timed.run(max(4, steps // 4), max(4, warmup // 4) if warmup else 0)
+    mm = kernel_times(matmul, max(8, steps // 4))
+    flops = 2.0 * wl.routed_rows * wl.n * wl.k
+    avg = float(np.mean(mm))
+    res.update({
+        "flops": flops,
+        "tflops": flops / (res["gpu_ms_per_step"] * 1e-3) / 1e12,
+        "grouped_ms": {"avg": avg, **_percentiles(mm), "n": len(mm)},
+        "grouped_tflops": flops / (avg * 1e-3) / 1e12,
+    })
+    # Direct on the same inputs, for the route comparison (not the headline)
+    dm = kernel_times(lambda i: matmul(i, B.DIRECT), 3)
+    res["direct_tflops"] = flops / (float(np.median(dm)) * 1e-3) / 1e12
+    del weights
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------- CPU oracle
+def cpu_baseline(budget_s: float = 15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the decode workload:
+    whole decode steps (route, the 8 routed rows' matmul, combine) repeated
+    until the budget is spent; one host thread."""
+    import oracle
+
+    wl = W.WORKLOADS["decode"]
+    logits = W.router_logits(wl)
+    bias = W.router_bias(wl)
+    x = W.activations(wl)
+    ids, _, _, _ = oracle.route(logits, bias, wl.top_k)
+    # the touched experts packed at indices 0..7 (placement does not change y)
+    packed = np.concatenate([W.expert_weights(wl, int(e)).contiguous().view(torch.uint8).numpy().reshape(-1)
+                             for e in ids[0]])
+    local_ids = np.arange(wl.top_k, dtype=np.uint32)[None]
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        ids_s, gates_s, _, _ = oracle.route(logits, bias, wl.top_k)
+        y = oracle.matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.top_k, wl.stride, wl.layout,
+                             packed, x, local_ids)
+        oracle.combine(y, gates_s, wl.top_k)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = (time.perf_counter() - t0) / n
+    touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
+    return {"value": touched / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole decode steps (route + 8x1536x4096 bf16 matmul + combine), "
+                      f"{dt * 1e3:.0f} ms each, 1 thread, {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the expert-ID matmul path here has no multi-GPU "
+              "form (sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    lib = B.load()
+    print(f"[bench] decode: {args.steps} steps, warmup {args.warmup}", file=sys.stderr, flush=True)
+    dec = bench_decode(lib, args.steps, args.warmup)
+    prefill = {}
+    if not args.no_prefill:
+        for name in ("down_proj", "prefill_balanced", "prefill_skewed"):
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            prefill[name] = bench_prefill(lib, name, args.steps, args.warmup)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+    d = dec["direct_ms"]["avg"] * 1e-3
+    line = {
+        "metric": "expert-ID matmul: decode weight GB/s (m=1) + prefill TFLOP/s (m=2048) at 1 GPU",
+        "value": round(dec["value_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": dec["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["gpu_ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode: m=1 k=4096 n=1536 n_experts=256 top_k=8, bf16 weights, "
+                               "f32 activations, sigmoid+bias routing, cold experts",
+                   "weights": "bf16", "m": 1, "n": 1536, "k": 4096, "n_experts": 256, "top_k": 8},
+        "roofline": {"kernel": "direct_kernel<bf16>", "bound": "hbm",
+                     "achieved": round(dec["touched_bytes"] / d / 1e9, 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(dec["touched_bytes"] / d / HBM_PEAK, 4),
+                     "traffic": None},
+        "decode_detail": dec,
+        "prefill": {k: {"tflops_step": round(v["tflops"], 2),
+                        "tflops_matmul": round(v["grouped_tflops"], 2),
+                        "frac_f32_peak_matmul": round(v["grouped_tflops"] * 1e12 / F32_PEAK, 4),
+                        "ms_per_step": round(v["gpu_ms_per_step"], 4),
+                        "matmul_ms": v["grouped_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
+                    for k, v in prefill.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+"""ctypes binding of libeidm.so (include/eidm.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors are torch CUDA tensors (device memory); the stream is the
+caller's current torch stream unless one is given.  The binding refuses to
+run when the library is missing -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libeidm.so")
+
+F32, F16, BF16 = 0, 1, 2
+SHARED_PER_TOKEN, SLOTTED = 0, 1
+DISTINCT_PER_TOKEN, MAY_REPEAT = 0, 1
+AUTO, DIRECT, GROUPED = 0, 1, 2
+OK, E_INVALID, E_UNSUPPORTED, E_SIZE, E_ALIGN, E_DEVICE = 0, -1, -2, -3, -4, -5
+
+EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk", "eidm_map",
+           "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward"]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("weight_dtype", ctypes.c_int32),
+                ("m", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("top_k", ctypes.c_uint32), ("n_experts", ctypes.c_uint32),
+                ("reserved0", ctypes.c_uint32), ("expert_stride_bytes", ctypes.c_uint64),
+                ("input_layout", ctypes.c_int32), ("id_multiplicity", ctypes.c_int32)]
+
+
+class Requirements(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("route", ctypes.c_int32),
+                ("required_weight_bytes", ctypes.c_uint64), ("input_elements", ctypes.c_uint64),
+                ("ids_elements", ctypes.c_uint64), ("output_elements", ctypes.c_uint64),
+                ("scratch_bytes", ctypes.c_uint64), ("grouped_legal", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
+
+
+class EidmError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"eidm error {code}: {message}")
+        self.code = code
+
+
+def make_shape(dtype: int, m: int, n: int, k: int, top_k: int, n_experts: int, stride: int,
+               layout: int = SHARED_PER_TOKEN, multiplicity: int = DISTINCT_PER_TOKEN) -> Shape:
+    return Shape(ctypes.sizeof(Shape), dtype, m, n, k, top_k, n_experts, 0, stride, layout,
+                 multiplicity)
+
+
+def shape_of(wl) -> Shape:
+    """Shape key of a workloads.Workload."""
+    return make_shape(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout,
+                      wl.multiplicity)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(name: str, t, elements: int, itemsize: int = 4, optional: bool = False) -> None:
+    """Refuse host tensors and tensors smaller than the call will touch."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):
+        return  # a raw device address: the caller vouches for it
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(t) < elements * itemsize:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, the call needs {elements * itemsize}")
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Library:
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first (python -m expert_id_matmul_amd.build)")
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        P, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
+        L.eidm_abi_version.restype = i32
+        L.eidm_abi_version.argtypes = []
+        L.eidm_last_error.restype = ctypes.c_char_p
+        L.eidm_last_error.argtypes = []
+        L.eidm_query.restype = i32
+        L.eidm_query.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(Requirements)]
+        L.eidm_route_topk.restype = i32
+        L.eidm_route_topk.argtypes = [P, P, u32, u32, u32, i32, P, P, P]
+        L.eidm_map.restype = i32
+        L.eidm_map.argtypes = [P, u32, u32, u32, P, P, P, P, u64, P]
+        L.eidm_map_scratch_bytes.restype = u64
+        L.eidm_map_scratch_bytes.argtypes = [u32, u32, u32]
+        L.eidm_matmul_id.restype = i32
+        L.eidm_matmul_id.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, P, u64, P,
+                                     ctypes.POINTER(ctypes.c_int)]
+        L.eidm_combine.restype = i32
+        L.eidm_combine.argtypes = [u32, u32, u32, P, P, P, P]
+        L.eidm_moe_forward.restype = i32
+        L.eidm_moe_forward.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, i32, P, P, P, P,
+                                       P, u64, P, ctypes.POINTER(ctypes.c_int)]
+
+    # ------------------------------------------------------------------ helpers
+    def _check(self, rc: int) -> None:
+        if rc != OK:
+            raise EidmError(rc, self.lib.eidm_last_error().decode())
+
+    def last_error(self) -> str:
+        return self.lib.eidm_last_error().decode()
+
+    def abi_version(self) -> int:
+        return self.lib.eidm_abi_version()
+
+    def _check_matmul_buffers(self, shape, route, weights, weight_bytes, input, ids, output,
+                              scratch) -> None:
+        req = self.query(shape, route)
+        _need("weights", weights, weight_bytes, 1)
+        _need("input", input, req.input_elements)
+        _need("ids", ids, req.ids_elements)
+        _need("output", output, req.output_elements)
+        if scratch is not None:
+            _need("scratch", scratch, 0, 1)
+
+    # ------------------------------------------------------------------ ABI calls
+    def query(self, shape: Shape, route: int = AUTO) -> Requirements:
+        req = Requirements()
+        req.struct_size = ctypes.sizeof(Requirements)
+        self._check(self.lib.eidm_query(ctypes.byref(shape), route, ctypes.byref(req)))
+        return req
+
+    def route_topk(self, logits, bias, top_k: int, ids, gates, renormalize: bool = True,
+                   stream=None) -> None:
+        m, n_experts = logits.shape
+        _need("logits", logits, m * n_experts)
+        _need("bias", bias, n_experts, optional=True)
+        _need("ids", ids, m * top_k)
+        _need("gates", gates, m * top_k, optional=True)
+        self._check(self.lib.eidm_route_topk(_ptr(logits), _ptr(bias), m, n_experts, top_k,
+                                             int(renormalize), _ptr(ids), _ptr(gates),
+                                             _stream(stream)))
+
+    def map_scratch_bytes(self, m: int, top_k: int, n_experts: int) -> int:
+        return int(self.lib.eidm_map_scratch_bytes(m, top_k, n_experts))
+
+    def map(self, ids, n_experts: int, counts, offsets, rows, scratch, stream=None) -> None:
+        m, top_k = ids.shape
+        _need("ids", ids, m * top_k)
+        _need("counts", counts, n_experts + 1)
+        _need("offsets", offsets, n_experts + 2)
+        _need("rows", rows, m * top_k)
+        _need("scratch", scratch, self.map_scratch_bytes(m, top_k, n_experts), 1)
+        nbytes = _nbytes(scratch)
+        self._check(self.lib.eidm_map(_ptr(ids), m, top_k, n_experts, _ptr(counts), _ptr(offsets),
+                                      _ptr(rows), _ptr(scratch), nbytes, _stream(stream)))
+
+    def matmul_id(self, shape: Shape, route: int, weights, input, ids, output, scratch=None,
+                  weight_bytes: int | None = None, stream=None) -> int:
+        if weight_bytes is None:
+            weight_bytes = _nbytes(weights)
+        self._check_matmul_buffers(shape, route, weights, weight_bytes, input, ids, output, scratch)
+        sbytes = _nbytes(scratch) if scratch is not None else 0
+        taken = ctypes.c_int(-1)
+        self._check(self.lib.eidm_matmul_id(ctypes.byref(shape), route, _ptr(weights), weight_bytes,
+                                            _ptr(input), _ptr(ids), _ptr(output), _ptr(scratch),
+                                            sbytes, _stream(stream), ctypes.byref(taken)))
+        return taken.value
+
+    def combine(self, y, gates, out, stream=None) -> None:
+        m, top_k = gates.shape
+        n = y.shape[-1]
+        _need("y", y, m * top_k * n)
+        _need("gates", gates, m * top_k)
+        _need("out", out, m * n)
+        self._check(self.lib.eidm_combine(m, top_k, n, _ptr(y), _ptr(gates), _ptr(out),
+                                          _stream(stream)))
+
+    def moe_forward(self, shape: Shape, route: int, weights, input, logits, bias, ids, gates, y,
+                    out, scratch=None, renormalize: bool = True, weight_bytes: int | None = None,
+                    stream=None) -> int:
+        if weight_bytes is None:
+            weight_bytes = _nbytes(weights)
+        self._check_matmul_buffers(shape, route, weights, weight_bytes, input, ids, y, scratch)
+        _need("logits", logits, shape.m * shape.n_experts)
+        _need("bias", bias, shape.n_experts, optional=True)
+        _need("gates", gates, shape.m * shape.top_k)
+        _need("out", out, shape.m * shape.n)
+        sbytes = _nbytes(scratch) if scratch is not None else 0
+        taken = ctypes.c_int(-1)
+        self._check(self.lib.eidm_moe_forward(ctypes.byref(shape), route, _ptr(weights),
+                                              weight_bytes, _ptr(input), _ptr(logits), _ptr(bias),
+                                              int(renormalize), _ptr(ids), _ptr(gates), _ptr(y),
+                                              _ptr(out), _ptr(scratch), sbytes, _stream(stream),
+                                              ctypes.byref(taken)))
+        return taken.value
+
+
+_LIB: Library | None = None
+
+
+def load(path: str = LIB_PATH) -> Library:
+    global _LIB
+    if _LIB is None or _LIB.path != path:
+        _LIB = Library(path)
+    return _LIB

@@ -1,0 +1,49 @@
+// eidm_internal.hpp -- kernel launchers behind the C ABI (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eidm {
+
+// Largest expert count the kernels take (router state per lane, map tables).
+constexpr uint32_t kMaxExperts = 2048;
+
+// Rows handled by one block of the map kernels.
+constexpr uint32_t kMapChunk = 256;
+
+struct MatmulArgs {
+    int dtype;
+    uint32_t m, n, k, top_k, n_experts;
+    uint64_t stride;
+    int layout;                 // 0 shared per token, 1 slotted
+    const void* weights;
+    const float* input;
+    const uint32_t* ids;
+    float* output;
+    bool vec;                   // 16-byte aligned rows: vector loads allowed
+};
+
+// Device pointers into a Grouped scratch buffer.
+struct MapBuffers {
+    uint32_t* hist;     // [blocks][n_experts+1]
+    uint32_t* counts;   // [n_experts+1]
+    uint32_t* offsets;  // [n_experts+2]
+    uint32_t* rows;     // [m*top_k]
+};
+
+uint32_t map_blocks(uint64_t routed_rows);
+uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts);
+
+hipError_t launch_route(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,
+                        uint32_t top_k, int renormalize, uint32_t* ids, float* gates,
+                        hipStream_t stream);
+hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_experts,
+                      const MapBuffers& buf, hipStream_t stream);
+hipError_t launch_direct(const MatmulArgs& a, hipStream_t stream);
+hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
+                          hipStream_t stream);
+hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,
+                          const float* gates, float* out, hipStream_t stream);
+
+}  // namespace eidm

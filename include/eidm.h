@@ -1,0 +1,238 @@
+/*
+ * eidm.h -- C ABI of libeidm.so: the mixture-of-experts expert-ID matmul
+ * (matmul_id) path on one AMD Instinct MI355X (gfx950).
+ *
+ * The path, for m tokens each routed to top_k of n_experts experts:
+ *   1. route    sigmoid + selection-bias top-k router -> ids, gates
+ *   2. map      per-expert lists of routed rows (grouped form only)
+ *   3. matmul   y[r, :] = W[ids[r]] . x_row(r) for every routed row
+ *               r = t*top_k + s, in one of two forms that give identical
+ *               bits: Direct (one routed row at a time, weight streaming)
+ *               and Grouped (each expert's gathered rows as one tile job)
+ *   4. combine  out[t, :] = sum_s gate[t, s] * y[t*top_k + s, :]
+ *
+ * Sources (docs.rs source views):
+ *   mlx-native 0.13.0, src/ops/dense_matmul_id_auto.rs -- the shape key
+ *     (struct DenseMatmulIdShape), the two routes and their required
+ *     bit identity (the value-independence theorem statement), the weight
+ *     extent and alignment checks (fn validate_cases), the input layouts,
+ *     id multiplicity and routing profiles (fn calibration_buffers), the
+ *     map pass and grouped scratch sized by (n_experts, m)
+ *     (fn expected_dispatches, DenseMatmulIdScratch::new).
+ *   cortiq-engine 0.7.7, src/mimo_moe.rs -- sigmoid + selection-bias
+ *     routing with renormalised gates p[e]/wsum (module doc, Dynamic::run,
+ *     the bank_tests model arch).
+ *   hf2q, src/inference/models/qwen35/dense_ffn_arena.rs -- routed-row
+ *     major ids/weights/y buffers and the weighted reduce (MoeFfnArena).
+ *
+ * Conventions (all entry points):
+ *   - Every pointer marked "device" is caller-owned device memory (for
+ *     example from hipMalloc or a torch CUDA tensor's data_ptr()).  The
+ *     library never allocates, frees or retains caller memory; buffers must
+ *     stay alive until the stream has passed the enqueued work.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; nothing synchronises.
+ *   - All arguments are validated on the host before anything is enqueued.
+ *     On any error the call returns a negative eidm_status, enqueues
+ *     nothing, and eidm_last_error() describes the failure.
+ *   - Sizes use overflow-checked products (an overflow is EIDM_E_INVALID).
+ *   - Entry points are reentrant; a scratch buffer belongs to one call in
+ *     flight at a time.
+ *   - Floating point: activations, gates and outputs are f32; weights are
+ *     native f32/f16/bf16, widened exactly to f32; every product is
+ *     accumulated with f32 fused multiply-add.
+ */
+#ifndef EIDM_H
+#define EIDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EIDM_ABI_VERSION 1
+
+/* Native weight scalar type (DenseMatmulIdShape.weight_dtype). */
+typedef enum eidm_dtype {
+    EIDM_DTYPE_F32 = 0,
+    EIDM_DTYPE_F16 = 1,
+    EIDM_DTYPE_BF16 = 2
+} eidm_dtype;
+
+/* Input rows: one per token shared by its top_k slots ([m, k]), or one per
+ * routed row ([m*top_k, k]) (DenseMatmulIdInputLayout). */
+typedef enum eidm_layout {
+    EIDM_LAYOUT_SHARED_PER_TOKEN = 0,
+    EIDM_LAYOUT_SLOTTED = 1
+} eidm_layout;
+
+/* Whether one token's top_k ids are distinct (DenseMatmulIdMultiplicity). */
+typedef enum eidm_multiplicity {
+    EIDM_IDS_DISTINCT_PER_TOKEN = 0,
+    EIDM_IDS_MAY_REPEAT = 1
+} eidm_multiplicity;
+
+/* Which form of the matmul runs (DenseMatmulIdRoute, plus AUTO). */
+typedef enum eidm_route {
+    EIDM_ROUTE_AUTO = 0,
+    EIDM_ROUTE_DIRECT = 1,
+    EIDM_ROUTE_GROUPED = 2
+} eidm_route;
+
+typedef enum eidm_status {
+    EIDM_OK = 0,
+    EIDM_E_INVALID = -1,     /* zero dimension, bad enum, null pointer, overflow */
+    EIDM_E_UNSUPPORTED = -2, /* route not legal for the shape                    */
+    EIDM_E_SIZE = -3,        /* weight extent or scratch too small              */
+    EIDM_E_ALIGN = -4,       /* pointer or stride misaligned for its type        */
+    EIDM_E_DEVICE = -5       /* a HIP call failed                                */
+} eidm_status;
+
+/*
+ * The full shape key of one matmul_id case (DenseMatmulIdShape: weight
+ * dtype, m, n, k, top_k, n_experts, expert stride, input layout, id
+ * multiplicity).  Expert e's weight matrix is [n, k], row-major (k
+ * contiguous), starting at byte e * expert_stride_bytes of the weight
+ * buffer; the stride may include padding.  struct_size must be
+ * sizeof(eidm_shape).
+ */
+typedef struct eidm_shape {
+    uint32_t struct_size;
+    int32_t weight_dtype;        /* eidm_dtype */
+    uint32_t m;                  /* tokens                     */
+    uint32_t n;                  /* output columns per row     */
+    uint32_t k;                  /* reduction length           */
+    uint32_t top_k;              /* routed rows per token      */
+    uint32_t n_experts;
+    uint32_t reserved0;          /* must be 0                  */
+    uint64_t expert_stride_bytes;
+    int32_t input_layout;        /* eidm_layout                */
+    int32_t id_multiplicity;     /* eidm_multiplicity          */
+} eidm_shape;
+
+/* What one case needs from the caller (host-only query). */
+typedef struct eidm_requirements {
+    uint32_t struct_size;        /* set by the caller: sizeof(eidm_requirements) */
+    int32_t route;               /* the route the query resolved to             */
+    uint64_t required_weight_bytes; /* (n_experts-1)*stride + n*k*sizeof(dtype)  */
+    uint64_t input_elements;     /* f32: m*k (shared) or m*top_k*k (slotted)    */
+    uint64_t ids_elements;       /* u32: m*top_k                                */
+    uint64_t output_elements;    /* f32: m*top_k*n                              */
+    uint64_t scratch_bytes;      /* device scratch the route needs (0: none)    */
+    int32_t grouped_legal;       /* 1 when the Grouped route accepts the shape  */
+    int32_t reserved0;
+} eidm_requirements;
+
+/* ABI version of the loaded library (EIDM_ABI_VERSION it was built with). */
+int eidm_abi_version(void);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* eidm_last_error(void);
+
+/*
+ * Host-only: validate `shape` and report its buffer sizes and the scratch
+ * the route needs.  `route` may be AUTO (the answer names the route AUTO
+ * picks when given that scratch).  Dimensions must be non-zero, the stride
+ * must cover one expert (n*k*size bytes) and be a multiple of the dtype
+ * size, top_k <= n_experts for distinct ids.  Grouped is legal for both
+ * multiplicities.  Enqueues nothing.
+ */
+int eidm_query(const eidm_shape* shape, int route, eidm_requirements* out);
+
+/*
+ * Router (cortiq-engine mimo_moe.rs: module doc, Dynamic::run and the
+ * bank_tests arch with router_sigmoid and norm_topk_prob):
+ *   s[t,e]   = sigmoid(logits[t,e]), rounded to f32
+ *   sel[t,e] = s[t,e] + bias[e]  (one f32 add; bias may be NULL = 0)
+ *   ids[t,j] = j-th largest sel of token t (j = 0..top_k-1); equal sel
+ *              keeps the lower expert index first; ids are distinct
+ *   gates[t,j] = s[t,ids[t,j]] / sum_j' s[t,ids[t,j']] (f32, sum in slot
+ *              order) when renormalize != 0, else s[t,ids[t,j]]
+ * logits: device f32 [m, n_experts]; bias: device f32 [n_experts] or NULL;
+ * ids: device u32 [m, top_k]; gates: device f32 [m, top_k] (may be NULL).
+ * Requires 1 <= top_k <= n_experts <= 2048.  Logits must be finite (a NaN
+ * logit ranks below every finite one; the ids stay distinct and in range).
+ */
+int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,
+                    uint32_t top_k, int renormalize, uint32_t* ids, float* gates, void* stream);
+
+/*
+ * Id -> row map (the map pass of the grouped route, mlx-native
+ * dense_matmul_id_auto.rs fn expected_dispatches): a stable counting sort
+ * of the routed rows r = 0..m*top_k-1 by key min(ids[r], n_experts).
+ *   counts  device u32 [n_experts+1]: rows per key (key n_experts = ids that
+ *           name no expert)
+ *   offsets device u32 [n_experts+2]: exclusive prefix sums of counts
+ *   rows    device u32 [m*top_k]: the rows, grouped by key, ascending
+ *           within each key
+ *   scratch device, >= eidm_map_scratch_bytes(m, top_k, n_experts) bytes,
+ *           4-byte aligned (per-block histograms)
+ * Results are exact and deterministic.  Requires m*top_k < 2^31 and
+ * n_experts <= 2048.
+ */
+int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
+             uint32_t* counts, uint32_t* offsets, uint32_t* rows, void* scratch,
+             uint64_t scratch_bytes, void* stream);
+
+/* Host-only: scratch bytes eidm_map needs (0 if m*top_k overflows). */
+uint64_t eidm_map_scratch_bytes(uint32_t m, uint32_t top_k, uint32_t n_experts);
+
+/*
+ * The expert-ID matmul (mlx-native dense_matmul_id_auto.rs: the shape key,
+ * the routes, the value-independence theorem statement):
+ *   y[r, j] = sum_c widen(W_e[j, c]) * x_row(r)[c],  e = ids[r],
+ *   r = t*top_k + s,  x_row(r) = input[t] (shared) or input[r] (slotted).
+ * weights      device, >= required_weight_bytes, aligned to the dtype size
+ * weight_bytes the extent the caller vouches for (checked against the shape)
+ * input        device f32 [input_elements]
+ * ids          device u32 [m, top_k]
+ * output       device f32 [m*top_k, n]; every element is overwritten and
+ *              nothing past it is written
+ * scratch      device, >= scratch_bytes from eidm_query for the route (may
+ *              be NULL for Direct); 256-byte aligned
+ * route_taken  (optional host int*) receives the route that ran
+ * Both routes give bit-identical outputs for the same inputs.  The
+ * reduction over k is the same fixed order in both: k is cut into granules
+ * of 8; granule g belongs to slice g mod 16; each slice accumulates its
+ * products in ascending k with f32 fma from +0; the 16 slice sums are added
+ * pairwise as (s, s+8), then (s, s+4), (s, s+2), (s, s+1).
+ * An id >= n_experts makes its output row quiet NaN (no weights are read).
+ * AUTO runs Grouped when it is legal, scratch covers it and the routed rows
+ * average at least 2 per expert (m*top_k >= 2*n_experts); Direct otherwise.
+ */
+int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint64_t weight_bytes,
+                   const float* input, const uint32_t* ids, float* output, void* scratch,
+                   uint64_t scratch_bytes, void* stream, int* route_taken);
+
+/*
+ * Gate-weighted sum over slots (cortiq-engine mimo_moe.rs Dynamic::run;
+ * hf2q dense_ffn_arena.rs MoeFfnArena's weighted reduce):
+ *   out[t, j] = sum_s gates[t, s] * y[t*top_k + s, j]
+ * accumulated with f32 fma from +0 in ascending s.
+ * y device f32 [m*top_k, n]; gates device f32 [m, top_k]; out device f32
+ * [m, n] (must not overlap y).
+ */
+int eidm_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const float* gates,
+                 float* out, void* stream);
+
+/*
+ * The whole path in one call: route (eidm_route_topk) -> matmul
+ * (eidm_matmul_id) -> combine (eidm_combine), enqueued in order on
+ * `stream`.  logits device f32 [m, n_experts]; bias device f32
+ * [n_experts] or NULL; ids/gates/y/out are caller buffers that receive the
+ * intermediate and final results.  shape->id_multiplicity must be
+ * DISTINCT_PER_TOKEN (the router's ids are distinct).
+ */
+int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights,
+                     uint64_t weight_bytes, const float* input, const float* logits,
+                     const float* bias, int renormalize, uint32_t* ids, float* gates, float* y,
+                     float* out, void* scratch, uint64_t scratch_bytes, void* stream,
+                     int* route_taken);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EIDM_H */

@@ -1,0 +1,149 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host before any launch
+(so none of these tests touches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_id_matmul_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eidm.h")
+
+# never dereferenced: every call below fails validation first
+FAKE = 0x7F0000000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eidm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_what_the_binding_uses():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib.lib, name), name
+    assert lib.abi_version() == 1
+
+
+def test_struct_sizes_match_the_header_layout():
+    assert ctypes.sizeof(B.Shape) == 48
+    assert ctypes.sizeof(B.Requirements) == 56
+
+
+def test_query_reports_the_pages_weight_extent_and_sizes(lib):
+    # mlx-native dense_matmul_id_auto.rs, A-B-A test: n=5, k=7, 4 experts,
+    # stride 152 -> a 596-byte weight buffer
+    s = B.make_shape(B.F32, 3, 5, 7, 3, 4, 152)
+    r = lib.query(s, B.DIRECT)
+    assert r.required_weight_bytes == 596
+    assert r.input_elements == 3 * 7 and r.ids_elements == 9 and r.output_elements == 9 * 5
+    assert r.route == B.DIRECT and r.scratch_bytes == 0 and r.grouped_legal == 1
+    g = lib.query(s, B.GROUPED)
+    assert g.route == B.GROUPED and g.scratch_bytes > 0
+    slotted = lib.query(B.make_shape(B.F32, 3, 5, 7, 3, 4, 152, B.SLOTTED), B.DIRECT)
+    assert slotted.input_elements == 9 * 7
+
+
+def test_query_auto_picks_direct_for_decode_and_grouped_for_prefill(lib):
+    dec = B.make_shape(B.BF16, 1, 1536, 4096, 8, 256, 1536 * 4096 * 2)
+    assert lib.query(dec, B.AUTO).route == B.DIRECT
+    pre = B.make_shape(B.BF16, 512, 768, 2048, 8, 128, 768 * 2048 * 2)
+    assert lib.query(pre, B.AUTO).route == B.GROUPED
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("m", 0, B.E_INVALID), ("n", 0, B.E_INVALID), ("k", 0, B.E_INVALID),
+    ("top_k", 0, B.E_INVALID), ("n_experts", 0, B.E_INVALID),
+    ("weight_dtype", 7, B.E_INVALID), ("input_layout", 2, B.E_INVALID),
+    ("id_multiplicity", 5, B.E_INVALID), ("reserved0", 1, B.E_INVALID),
+    ("struct_size", 40, B.E_INVALID), ("top_k", 5, B.E_INVALID),  # 5 distinct of 4
+    ("expert_stride_bytes", 139, B.E_ALIGN),  # not a multiple of 4
+    ("expert_stride_bytes", 136, B.E_INVALID),  # shorter than one expert (140 B)
+    ("n_experts", 4096, B.E_UNSUPPORTED),
+    ("m", 2 ** 31, B.E_UNSUPPORTED),
+])
+def test_query_rejects_bad_shapes(lib, field, value, code):
+    s = B.make_shape(B.F32, 3, 5, 7, 3, 4, 152)
+    setattr(s, field, value)
+    with pytest.raises(B.EidmError) as ei:
+        lib.query(s, B.DIRECT)
+    assert ei.value.code == code, lib.last_error()
+    assert lib.last_error()
+
+
+def test_query_rejects_overflowing_extents(lib):
+    s = B.make_shape(B.F32, 1, 65536, 65536, 1, 2000, 2 ** 62)
+    with pytest.raises(B.EidmError) as ei:
+        lib.query(s, B.DIRECT)
+    assert ei.value.code == B.E_INVALID
+
+
+def test_may_repeat_allows_top_k_above_n_experts(lib):
+    s = B.make_shape(B.F32, 3, 5, 7, 6, 4, 152, B.SHARED_PER_TOKEN, B.MAY_REPEAT)
+    assert lib.query(s, B.GROUPED).grouped_legal == 1
+
+
+def test_unknown_route_is_rejected(lib):
+    with pytest.raises(B.EidmError):
+        lib.query(B.make_shape(B.F32, 3, 5, 7, 3, 4, 152), 9)
+
+
+def _matmul(lib, shape, route=B.DIRECT, weights=FAKE, wbytes=596, inp=FAKE, ids=FAKE,
+            out=FAKE, scratch=0, sbytes=0):
+    taken = ctypes.c_int(-1)
+    rc = lib.lib.eidm_matmul_id(ctypes.byref(shape), route, ctypes.c_void_p(weights), wbytes,
+                                ctypes.c_void_p(inp), ctypes.c_void_p(ids), ctypes.c_void_p(out),
+                                ctypes.c_void_p(scratch), sbytes, None, ctypes.byref(taken))
+    return rc, taken.value
+
+
+def test_matmul_rejects_before_launch(lib):
+    s = B.make_shape(B.F32, 3, 5, 7, 3, 4, 152)
+    # short weight extent (595 < 596)
+    assert _matmul(lib, s, wbytes=595) == (B.E_SIZE, -1)
+    # weights misaligned for f32
+    assert _matmul(lib, s, weights=FAKE + 2)[0] == B.E_ALIGN
+    # null pointers
+    assert _matmul(lib, s, weights=0)[0] == B.E_INVALID
+    assert _matmul(lib, s, out=0)[0] == B.E_INVALID
+    assert _matmul(lib, s, ids=FAKE + 1)[0] == B.E_ALIGN
+    # grouped without scratch / with too little / misaligned
+    assert _matmul(lib, s, route=B.GROUPED)[0] == B.E_SIZE
+    assert _matmul(lib, s, route=B.GROUPED, scratch=FAKE, sbytes=8)[0] == B.E_SIZE
+    need = lib.query(s, B.GROUPED).scratch_bytes
+    assert _matmul(lib, s, route=B.GROUPED, scratch=FAKE + 64, sbytes=need)[0] == B.E_ALIGN
+    # bf16 weights need 2-byte alignment only
+    sb = B.make_shape(B.BF16, 9, 11, 37, 6, 8, 832)
+    assert _matmul(lib, sb, weights=FAKE + 3, wbytes=10 ** 6)[0] == B.E_ALIGN
+
+
+def test_route_map_combine_reject_bad_arguments(lib):
+    L = lib.lib
+    P = ctypes.c_void_p
+    assert L.eidm_route_topk(P(FAKE), None, 4, 8, 9, 1, P(FAKE), None, None) == B.E_INVALID
+    assert L.eidm_route_topk(P(FAKE), None, 0, 8, 2, 1, P(FAKE), None, None) == B.E_INVALID
+    assert L.eidm_route_topk(None, None, 4, 8, 2, 1, P(FAKE), None, None) == B.E_INVALID
+    assert L.eidm_route_topk(P(FAKE), None, 4, 4096, 2, 1, P(FAKE), None, None) == B.E_UNSUPPORTED
+    assert L.eidm_route_topk(P(FAKE + 2), None, 4, 8, 2, 1, P(FAKE), None, None) == B.E_ALIGN
+    assert L.eidm_combine(0, 2, 8, P(FAKE), P(FAKE), P(FAKE), None) == B.E_INVALID
+    assert L.eidm_combine(2, 2, 8, None, P(FAKE), P(FAKE), None) == B.E_INVALID
+    assert L.eidm_combine(2, 2, 8, P(FAKE + 1), P(FAKE), P(FAKE), None) == B.E_ALIGN
+    need = lib.map_scratch_bytes(10, 2, 8)
+    assert need == 9 * 4  # one block of rows, n_experts + 1 counters
+    assert L.eidm_map(P(FAKE), 10, 2, 8, P(FAKE), P(FAKE), P(FAKE), P(FAKE), need - 4, None) == B.E_SIZE
+    assert L.eidm_map(P(FAKE), 10, 2, 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), need, None) == B.E_INVALID
+
+
+def test_moe_forward_requires_distinct_ids(lib):
+    s = B.make_shape(B.F32, 3, 5, 7, 3, 4, 152, B.SHARED_PER_TOKEN, B.MAY_REPEAT)
+    P = ctypes.c_void_p
+    rc = lib.lib.eidm_moe_forward(ctypes.byref(s), B.DIRECT, P(FAKE), 596, P(FAKE), P(FAKE), None, 1,
+                                  P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 0, None, None)
+    assert rc == B.E_INVALID

@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (per element): matmul outputs and combined outputs within
+|gpu - oracle| / max(1, |oracle|) <= 2e-5; router ids and the id map bit
+exact; renormalised gates within 2e-6; Direct and Grouped bit identical on
+every shape, and both equal to the CPU evaluation of the documented f32
+reduction order bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_id_matmul_amd import binding as B
+from expert_id_matmul_amd import workloads as W
+
+from helpers import (GATE_TOL, GUARD, assert_close, canonical_matmul_id, check_guarded,
+                     ids_to_dev, poisoned_output, to_dev, u32)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _wl(name, dtype, m, n, k, top_k, n_experts, stride=None, layout=W.LAYOUT_SHARED,
+        mult=W.IDS_DISTINCT, seed=7, ids_kind="random"):
+    size = W.DTYPE_SIZE[dtype]
+    return W.Workload(name, dtype, m, n, k, top_k, n_experts, stride or n * k * size, layout, mult,
+                      seed, 0.5 if dtype == W.DT_F32 else 0.05, ids_kind, "softmax")
+
+
+# small cases: several tiles and rounds plus ragged tails in n, k and rows
+SMALL = [
+    W.WORKLOADS["tiny"],
+    # the page's test_shape: bf16, 9 tokens, n=11, k=37, top-6 of 8, padded 832-byte stride
+    _wl("page_test_shape", W.DT_BF16, 9, 11, 37, 6, 8, stride=832, seed=11),
+    # the page's A-B-A case: f32 n=5 k=7 top-3 of 4, 152-byte stride
+    _wl("page_aba", W.DT_F32, 3, 5, 7, 3, 4, stride=152, seed=12),
+] + [
+    # the page's injected-failure shapes: f32, 5 experts, top-3
+    _wl(f"page_inject_m{m}", W.DT_F32, m, n, k, 3, 5, seed=100 + m)
+    for (m, n, k) in [(13, 31, 47), (14, 33, 49), (15, 35, 51), (16, 37, 53), (17, 39, 55), (18, 41, 57)]
+] + [
+    _wl(f"mix_{W.DTYPE_NAME[dt]}_{'slot' if lay else 'shared'}", dt, 37, 70, 300, 3, 9,
+        stride=70 * 300 * W.DTYPE_SIZE[dt] + 64, layout=lay, seed=20 + dt * 2 + lay)
+    for dt in (W.DT_F32, W.DT_F16, W.DT_BF16) for lay in (W.LAYOUT_SHARED, W.LAYOUT_SLOTTED)
+] + [
+    _wl("vec_bf16", W.DT_BF16, 33, 96, 512, 4, 16, seed=30),
+    _wl("vec_f16_slot_tail", W.DT_F16, 20, 64, 264, 8, 16, layout=W.LAYOUT_SLOTTED, seed=31),
+    _wl("vec_f32", W.DT_F32, 40, 72, 392, 2, 6, seed=32),
+    _wl("k_below_granule", W.DT_BF16, 5, 9, 5, 2, 3, seed=33),
+    _wl("n1_k1", W.DT_F32, 4, 1, 1, 2, 3, seed=34),
+    _wl("one_expert_top1", W.DT_F16, 17, 40, 96, 1, 1, seed=35),
+    _wl("m1_decode_like", W.DT_BF16, 1, 136, 1024, 8, 64, seed=36),
+    _wl("may_repeat", W.DT_BF16, 12, 48, 256, 5, 3, mult=W.IDS_MAY_REPEAT, seed=37, ids_kind="repeat"),
+]
+
+
+def _ids(wl):
+    if wl.ids_kind == "repeat":
+        rng = np.random.default_rng(wl.seed)
+        return rng.integers(0, wl.n_experts, size=(wl.m, wl.top_k)).astype(np.uint32)
+    return W.ids(wl)
+
+
+def run_matmul(lib, wl, wdev, x, ids, route, allow_nan=False):
+    out = poisoned_output(wl.routed_rows * wl.n)
+    scratch = None
+    if route == B.GROUPED:
+        need = lib.query(B.shape_of(wl), B.GROUPED).scratch_bytes
+        scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+    taken = lib.matmul_id(B.shape_of(wl), route, wdev, to_dev(x), ids_to_dev(ids), out, scratch,
+                          weight_bytes=wl.weight_bytes)
+    assert taken == route
+    torch.cuda.synchronize()
+    return check_guarded(out, wl.routed_rows * wl.n, allow_nan).reshape(wl.routed_rows, wl.n)
+
+
+def _oracle_y(wl, wb, x, ids):
+    return oracle.matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout,
+                            wb, x, ids)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_matmul_small_parity_and_bit_identity(lib, wl):
+    print(f"[case] matmul {wl.name}", flush=True)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    ids = _ids(wl)
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32)), "Direct and Grouped differ"
+    assert_close(yd, _oracle_y(wl, wb, x, ids), what=wl.name)
+    canon = canonical_matmul_id(wl, wb, x, ids)
+    assert np.array_equal(yd.view(np.uint32), canon.view(np.uint32)), "not the documented order"
+
+
+@pytest.mark.parametrize("profile", ["balanced", "skewed", "repeat"])
+def test_bit_identity_on_the_pages_calibration_inputs(lib, profile):
+    """Adversarial activations and the balanced / maximally skewed / repeating
+    id profiles of the page's calibration (fn calibration_buffers)."""
+    print(f"[case] calibration profile {profile}", flush=True)
+    mult = W.IDS_MAY_REPEAT if profile == "repeat" else W.IDS_DISTINCT
+    wl = _wl("calib", W.DT_BF16, 64, 100, 640, 6, 24, mult=mult, seed=40)
+    wb = W.weight_bytes(wl)
+    x = W.adversarial_activations(wl.m, wl.k)
+    ids = W.profile_ids(wl.m, wl.top_k, wl.n_experts, profile)
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32))
+    assert_close(yd, _oracle_y(wl, wb, x, ids), what=profile)
+    assert np.array_equal(yd.view(np.uint32), canonical_matmul_id(wl, wb, x, ids).view(np.uint32))
+
+
+def test_modular_fill_weights(lib):
+    """The page's deterministic f32 weight fill ((19 i + 37 seed) mod 257 - 128) / 263."""
+    wl = _wl("modfill", W.DT_F32, 13, 31, 47, 3, 5, seed=101)
+    wb = W.modular_fill(wl.n_experts * wl.n * wl.k, 101).view(np.uint8)
+    x = W.adversarial_activations(wl.m, wl.k)
+    ids = W.profile_ids(wl.m, 3, 5, "balanced")
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32))
+    assert_close(yd, _oracle_y(wl, wb, x, ids))
+
+
+def test_ids_naming_no_expert_give_nan_rows_in_both_routes(lib):
+    wl = _wl("bad_ids", W.DT_BF16, 10, 40, 200, 3, 6, seed=50)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    ids = W.ids(wl).copy()
+    ids[2, 1] = 6
+    ids[7, 0] = 0xFFFFFFFF
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT, allow_nan=True)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED, allow_nan=True)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32))
+    bad = [2 * 3 + 1, 7 * 3 + 0]
+    assert np.isnan(yd[bad]).all()
+    assert np.isfinite(np.delete(yd, bad, axis=0)).all()
+    assert_close(yd, _oracle_y(wl, wb, x, ids))
+
+
+def test_row_and_slot_permutation_permute_outputs_bitwise(lib):
+    wl = _wl("perm", W.DT_BF16, 24, 64, 384, 4, 12, seed=51)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    ids = W.ids(wl)
+    wdev = to_dev(wb)
+    perm = np.random.default_rng(1).permutation(wl.m)
+    for route in (B.DIRECT, B.GROUPED):
+        y = run_matmul(lib, wl, wdev, x, ids, route).reshape(wl.m, wl.top_k, wl.n)
+        yp = run_matmul(lib, wl, wdev, x[perm], ids[perm], route).reshape(wl.m, wl.top_k, wl.n)
+        assert np.array_equal(yp.view(np.uint32), y[perm].view(np.uint32))
+        sp = np.array([3, 1, 0, 2])
+        ys = run_matmul(lib, wl, wdev, x, ids[:, sp], route).reshape(wl.m, wl.top_k, wl.n)
+        assert np.array_equal(ys.view(np.uint32), y[:, sp].view(np.uint32))
+
+
+# ------------------------------------------------------------------ router
+@pytest.mark.parametrize("m,n_experts,top_k,with_bias", [
+    (300, 256, 8, True), (77, 8, 2, True), (64, 64, 6, False), (50, 100, 7, True),
+    (9, 2048, 8, True), (33, 128, 1, True), (5, 16, 16, True), (2, 1, 1, False),
+])
+def test_router_ids_exact_and_gates_close(lib, m, n_experts, top_k, with_bias):
+    print(f"[case] router m={m} E={n_experts} top_k={top_k}", flush=True)
+    logits = W.random_f32((m, n_experts), 60, m, n_experts)
+    bias = (W.random_f32((n_experts,), 61, n_experts) * 0.1).astype(np.float32) if with_bias else None
+    ids_o, gates_o, _, _ = oracle.route(logits, bias, top_k)
+    ids = torch.empty((m, top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((m, top_k), dtype=torch.float32, device="cuda")
+    lib.route_topk(to_dev(logits), None if bias is None else to_dev(bias), top_k, ids, gates)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(ids), ids_o)
+    g = gates.cpu().numpy().astype(np.float64)
+    assert float(np.max(np.abs(g - gates_o) / gates_o)) <= GATE_TOL
+
+
+def test_router_ties_and_raw_scores(lib):
+    logits = np.zeros((4, 32), np.float32)
+    logits[1, 7] = logits[1, 30] = 2.0
+    ids = torch.empty((4, 5), dtype=torch.int32, device="cuda")
+    gates = torch.empty((4, 5), dtype=torch.float32, device="cuda")
+    lib.route_topk(to_dev(logits), None, 5, ids, gates, renormalize=False)
+    torch.cuda.synchronize()
+    got = u32(ids)
+    assert list(got[0]) == [0, 1, 2, 3, 4]
+    assert list(got[1]) == [7, 30, 0, 1, 2]
+    ids_o, g_o, _, _ = oracle.route(logits, None, 5, renormalize=False)
+    assert np.array_equal(got, ids_o)
+    assert np.array_equal(gates.cpu().numpy().astype(np.float64), g_o)
+
+
+# ------------------------------------------------------------------ map
+@pytest.mark.parametrize("case", ["balanced", "skewed", "repeat", "random", "invalid", "large"])
+def test_map_is_exact(lib, case):
+    print(f"[case] map {case}", flush=True)
+    if case in ("balanced", "skewed", "repeat"):
+        m, top_k, E = 512, 8, 128
+        ids = W.profile_ids(m, top_k, E, case)
+    elif case == "large":
+        m, top_k, E = 2048, 8, 256
+        logits = W.random_f32((m, E), 70)
+        ids = oracle.route(logits, None, top_k)[0]
+    else:
+        m, top_k, E = 300, 5, 37
+        ids = np.random.default_rng(71).integers(0, E, size=(m, top_k)).astype(np.uint32)
+        if case == "invalid":
+            ids[5, 1] = E
+            ids[100, 4] = 0xFFFFFFFF
+            ids[299, 0] = 1000
+    counts = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 2, dtype=torch.int32, device="cuda")
+    rows = torch.empty(m * top_k, dtype=torch.int32, device="cuda")
+    scratch = torch.empty(lib.map_scratch_bytes(m, top_k, E), dtype=torch.uint8, device="cuda")
+    lib.map(ids_to_dev(ids), E, counts, offsets, rows, scratch)
+    torch.cuda.synchronize()
+    c_o, o_o, r_o = oracle.id_map(ids, E)
+    assert np.array_equal(u32(counts), c_o)
+    assert np.array_equal(u32(offsets), o_o)
+    assert np.array_equal(u32(rows), r_o)
+
+
+# ------------------------------------------------------------------ combine
+@pytest.mark.parametrize("m,top_k,n", [(7, 3, 33), (64, 8, 256), (1, 8, 1536), (5, 1, 2)])
+def test_combine_parity(lib, m, top_k, n):
+    y = W.random_f32((m * top_k, n), 80, m, n)
+    g = np.abs(W.random_f32((m, top_k), 81, m))
+    out = poisoned_output(m * n)
+    lib.combine(to_dev(y), to_dev(g), out)
+    torch.cuda.synchronize()
+    got = check_guarded(out, m * n).reshape(m, n)
+    assert_close(got, oracle.combine(y.astype(np.float64), g.astype(np.float64), top_k))
+
+
+def test_combine_one_hot_gates_copy_rows_bitwise(lib):
+    m, top_k, n = 6, 4, 40
+    y = W.random_f32((m * top_k, n), 82)
+    for j in range(top_k):
+        g = np.zeros((m, top_k), np.float32)
+        g[:, j] = 1.0
+        out = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        lib.combine(to_dev(y), to_dev(g), out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), y.reshape(m, top_k, n)[:, j].view(np.uint32))
+
+
+# ------------------------------------------------------------------ whole path
+@pytest.mark.parametrize("route", [B.DIRECT, B.GROUPED, B.AUTO])
+def test_moe_forward_small_down_projection(lib, route):
+    """Slotted input, f16 experts, sigmoid + bias routing, gate-weighted sum."""
+    wl = W.small("down_proj", m=48, n=96, k=200, n_experts=32, top_k=4)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    logits = W.router_logits(wl)
+    bias = W.router_bias(wl)
+    ids_o, gates_o, _, _ = oracle.route(logits, bias, wl.top_k)
+    y_o = _oracle_y(wl, wb, x, ids_o)
+    out_o = oracle.combine(y_o, gates_o, wl.top_k)
+    dev = lambda a: to_dev(a)
+    ids = torch.empty((wl.m, wl.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((wl.m, wl.top_k), dtype=torch.float32, device="cuda")
+    y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
+    out = poisoned_output(wl.m * wl.n)
+    need = lib.query(B.shape_of(wl), B.GROUPED).scratch_bytes
+    scratch = torch.empty(need, dtype=torch.uint8, device="cuda")
+    taken = lib.moe_forward(B.shape_of(wl), route, dev(wb), dev(x), dev(logits), dev(bias), ids,
+                            gates, y, out, scratch, weight_bytes=wl.weight_bytes)
+    torch.cuda.synchronize()
+    assert taken in (B.DIRECT, B.GROUPED)
+    assert np.array_equal(u32(ids), ids_o)
+    assert_close(y.cpu().numpy(), y_o, what="y")
+    assert_close(check_guarded(out, wl.m * wl.n).reshape(wl.m, wl.n), out_o, what="out")
