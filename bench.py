@@ -103,14 +103,25 @@ class Timed:
                 "wall_ms_per_step": wall * 1e3 / done}
 
 
-def kernel_times(call, steps: int):
-    """HIP events around `call(i)` for i < steps (eager, same stream)."""
+SPIN_CYCLES = 200_000  # ~80 us of GPU spin: the host enqueues the timed launch meanwhile
+
+
+def kernel_times(call, steps: int, before=None, after=None):
+    """HIP events around `call(i)` for i < steps, on the stream the kernels run
+    on.  A short GPU spin is queued ahead of each start event so the GPU is
+    still busy while the host enqueues event, launch and event: the interval
+    then holds the kernel alone, not the host's launch latency."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i in range(steps):
+        if before is not None:
+            before(i)
+        torch.cuda._sleep(SPIN_CYCLES)
         evs[i][0].record()
         call(i)
         evs[i][1].record()
+        if after is not None:
+            after(i)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in evs]
 
@@ -164,12 +175,7 @@ def bench_decode(lib, steps: int, warmup: int):
     assert torch.equal(graph_out, out) and torch.equal(graph_ids, ids), "graph replay differs from eager"
     assert sorted(graph_ids.cpu().numpy()[0].tolist()) == list(range(8 * (ROT - 1), 8 * ROT))
     # per-kernel: the Direct kernel alone, eager, between the same route/combine launches
-    direct_ms = []
-    for rep in range(max(1, steps // ROT)):
-        for i in range(ROT):
-            route(i)
-            direct_ms += kernel_times(lambda _: matmul(i), 1)
-            combine(i)
+    direct_ms = kernel_times(matmul, max(ROT, steps), before=route, after=combine)
     touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
     med = _percentiles(direct_ms)["median"]
     avg = float(np.mean(direct_ms))

@@ -239,6 +239,9 @@ int check_route_args(const float* logits, uint32_t m, uint32_t n_experts, uint32
         return fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", n_experts,
                     eidm::kMaxExperts);
     if (top_k > n_experts) return fail(EIDM_E_INVALID, "top_k %u above n_experts %u", top_k, n_experts);
+    if (top_k > eidm::kMaxRouterTopK)
+        return fail(EIDM_E_UNSUPPORTED, "router top_k %u above the supported %u", top_k,
+                    eidm::kMaxRouterTopK);
     uint64_t tmp;
     if (!mul_ok(m, n_experts, &tmp) || tmp > (1ull << 40)) return fail(EIDM_E_INVALID, "m*n_experts too large");
     if ((uint64_t)m + 3 > kIndexLimit * 4) return fail(EIDM_E_UNSUPPORTED, "m too large");

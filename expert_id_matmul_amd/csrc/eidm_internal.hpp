@@ -9,8 +9,8 @@ namespace eidm {
 // Largest expert count the kernels take (router state per lane, map tables).
 constexpr uint32_t kMaxExperts = 2048;
 
-// Rows handled by one block of the map kernels.
-constexpr uint32_t kMapChunk = 256;
+// Largest top_k the router takes (one pick per lane).
+constexpr uint32_t kMaxRouterTopK = 64;
 
 struct MatmulArgs {
     int dtype;
@@ -32,7 +32,8 @@ struct MapBuffers {
     uint32_t* rows;     // [m*top_k]
 };
 
-uint32_t map_blocks(uint64_t routed_rows);
+uint32_t map_waves(uint32_t n_experts);
+uint32_t map_blocks(uint64_t routed_rows, uint32_t n_experts);
 uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts);
 
 hipError_t launch_route(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,

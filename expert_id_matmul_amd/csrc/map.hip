@@ -7,7 +7,8 @@
 // by (n_experts, m).
 //
 // Key of routed row r: min(ids[r], n_experts) (the last bucket gathers ids
-// that name no expert).  Two passes over blocks of kMapChunk rows:
+// that name no expert).  Two passes over blocks of 64*W rows (W wavefronts,
+// as many as the per-wave count tables fit in 64 KB of LDS, at most 16):
 //   hist:    per block, rows per key (wave-aggregated LDS atomics);
 //   scatter: per block, global position of each row = rows of smaller keys
 //            + rows of the same key in earlier blocks + rows of the same key
@@ -20,7 +21,7 @@
 namespace eidm {
 namespace {
 
-constexpr int kMapWaves = kMapChunk / 64;
+constexpr int kMaxMapWaves = 16;
 
 __device__ __forceinline__ uint32_t key_of(uint32_t id, uint32_t n_experts) {
     return id < n_experts ? id : n_experts;
@@ -41,11 +42,12 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Exclusive scan of a[0..count) in LDS by the whole block (blockDim 256);
-// returns the total.  `wave_tot` is 4 words of LDS.
+// Exclusive scan of a[0..count) in LDS by the whole block; returns the
+// total.  `wave_tot` is one word of LDS per wavefront.
 __device__ uint32_t block_exclusive_scan(uint32_t* a, uint32_t count, uint32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t per = (count + 255) / 256;
+    const int waves = blockDim.x >> 6;
+    const uint32_t per = (count + blockDim.x - 1) / blockDim.x;
     const uint32_t begin = min(count, (uint32_t)tid * per);
     const uint32_t end = min(count, begin + per);
     uint32_t s = 0;
@@ -59,7 +61,7 @@ __device__ uint32_t block_exclusive_scan(uint32_t* a, uint32_t count, uint32_t* 
     if (lane == 63) wave_tot[wave] = inc;
     __syncthreads();
     uint32_t before = 0, total = 0;
-    for (int w = 0; w < kMapWaves; ++w) {
+    for (int w = 0; w < waves; ++w) {
         if (w < wave) before += wave_tot[w];
         total += wave_tot[w];
     }
@@ -73,7 +75,7 @@ __device__ uint32_t block_exclusive_scan(uint32_t* a, uint32_t count, uint32_t* 
     return total;
 }
 
-__global__ __launch_bounds__(kMapChunk) void map_hist_kernel(const uint32_t* __restrict__ ids,
+__global__ __launch_bounds__(64 * kMaxMapWaves) void map_hist_kernel(const uint32_t* __restrict__ ids,
                                                              uint32_t routed_rows,
                                                              uint32_t n_experts, int nbits,
                                                              uint32_t* __restrict__ hist) {
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(kMapChunk) void map_hist_kernel(const uint32_t* __r
     for (uint32_t i = threadIdx.x; i < buckets; i += blockDim.x) cnt[i] = 0;
     __syncthreads();
     const int lane = threadIdx.x & 63;
-    const uint32_t r = blockIdx.x * kMapChunk + threadIdx.x;
+    const uint32_t r = blockIdx.x * blockDim.x + threadIdx.x;
     const bool active = r < routed_rows;
     const uint32_t key = active ? key_of(ids[r], n_experts) : 0;
     const uint64_t same = same_key_lanes(key, nbits, active);
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kMapChunk) void map_hist_kernel(const uint32_t* __r
     for (uint32_t i = threadIdx.x; i < buckets; i += blockDim.x) out[i] = cnt[i];
 }
 
-__global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
+__global__ __launch_bounds__(64 * kMaxMapWaves) void map_scatter_kernel(
     const uint32_t* __restrict__ ids, uint32_t routed_rows, uint32_t n_experts, int nbits,
     uint32_t nblocks, const uint32_t* __restrict__ hist, uint32_t* __restrict__ counts,
     uint32_t* __restrict__ offsets, uint32_t* __restrict__ rows) {
@@ -100,12 +102,14 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
     const uint32_t buckets = n_experts + 1;
     uint32_t* base = lds;                       // [buckets]
     uint32_t* earlier = base + buckets;         // [buckets]
-    uint32_t* wcnt = earlier + buckets;         // [kMapWaves][buckets]
-    uint32_t* wave_tot = wcnt + kMapWaves * buckets;  // [4]
+    const int waves = blockDim.x >> 6;
+    uint32_t* wcnt = earlier + buckets;         // [waves][buckets]
+    uint32_t* wave_tot = wcnt + waves * buckets;  // [waves]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     for (uint32_t b = tid; b < buckets; b += blockDim.x) {
         uint32_t tot = 0, pre = 0;
+#pragma unroll 8
         for (uint32_t c = 0; c < nblocks; ++c) {
             const uint32_t h = hist[(size_t)c * buckets + b];
             tot += h;
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
         earlier[b] = pre;
         if (blockIdx.x == 0) counts[b] = tot;
     }
-    for (uint32_t i = tid; i < kMapWaves * buckets; i += blockDim.x) wcnt[i] = 0;
+    for (uint32_t i = tid; i < waves * buckets; i += blockDim.x) wcnt[i] = 0;
     __syncthreads();
     block_exclusive_scan(base, buckets, wave_tot);
     for (uint32_t b = tid; b < buckets; b += blockDim.x) {
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
     }
     if (blockIdx.x == 0 && tid == 0) offsets[buckets] = routed_rows;
 
-    const uint32_t r = blockIdx.x * kMapChunk + tid;
+    const uint32_t r = blockIdx.x * blockDim.x + tid;
     const bool active = r < routed_rows;
     const uint32_t key = active ? key_of(ids[r], n_experts) : 0;
     const uint64_t same = same_key_lanes(key, nbits, active);
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(kMapChunk) void map_scatter_kernel(
     __syncthreads();
     for (uint32_t b = tid; b < buckets; b += blockDim.x) {
         uint32_t run = 0;
-        for (int w = 0; w < kMapWaves; ++w) {
+        for (int w = 0; w < waves; ++w) {
             const uint32_t v = wcnt[w * buckets + b];
             wcnt[w * buckets + b] = run;
             run += v;
@@ -151,25 +155,35 @@ int key_bits(uint32_t n_experts) {
 
 }  // namespace
 
-uint32_t map_blocks(uint64_t routed_rows) {
-    return (uint32_t)((routed_rows + kMapChunk - 1) / kMapChunk);
+uint32_t map_waves(uint32_t n_experts) {
+    // (2 + W) count tables of n_experts+1 words plus W words within 64 KB
+    const uint32_t fit = 16384u / (n_experts + 2) - 2;
+    uint32_t w = 1;
+    while (w * 2 <= fit && w * 2 <= (uint32_t)kMaxMapWaves) w *= 2;
+    return w;
+}
+
+uint32_t map_blocks(uint64_t routed_rows, uint32_t n_experts) {
+    const uint32_t chunk = 64 * map_waves(n_experts);
+    return (uint32_t)((routed_rows + chunk - 1) / chunk);
 }
 
 uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts) {
-    return (uint64_t)map_blocks(routed_rows) * (n_experts + 1);
+    return (uint64_t)map_blocks(routed_rows, n_experts) * (n_experts + 1);
 }
 
 hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_experts,
                       const MapBuffers& buf, hipStream_t stream) {
-    const uint32_t blocks = map_blocks(routed_rows);
+    const uint32_t waves = map_waves(n_experts);
+    const uint32_t blocks = map_blocks(routed_rows, n_experts);
     const uint32_t buckets = n_experts + 1;
     const int nbits = key_bits(n_experts);
-    hipLaunchKernelGGL(map_hist_kernel, dim3(blocks), dim3(kMapChunk), buckets * sizeof(uint32_t),
+    hipLaunchKernelGGL(map_hist_kernel, dim3(blocks), dim3(64 * waves), buckets * sizeof(uint32_t),
                        stream, ids, routed_rows, n_experts, nbits, buf.hist);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const size_t lds = ((2 + kMapWaves) * (size_t)buckets + 4) * sizeof(uint32_t);
-    hipLaunchKernelGGL(map_scatter_kernel, dim3(blocks), dim3(kMapChunk), lds, stream, ids,
+    const size_t lds = ((2 + waves) * (size_t)buckets + waves) * sizeof(uint32_t);
+    hipLaunchKernelGGL(map_scatter_kernel, dim3(blocks), dim3(64 * waves), lds, stream, ids,
                        routed_rows, n_experts, nbits, blocks, buf.hist, buf.counts, buf.offsets,
                        buf.rows);
     return hipGetLastError();

@@ -10,45 +10,127 @@
 //
 // Every output goes through the same canonical order as in the Direct form
 // (eidm_device.hpp): the 16 blocks of each matrix-core step are the 16
-// k-slices, and within a block the 4 A-rows are 4 gathered routed rows and
-// the 4 B-columns are 4 output columns, so one step advances 16 outputs of
-// every slice at once.  A wavefront holds a (4R rows) x (4C columns) tile;
-// a block is 2x2 wavefronts.
+// k-slices; within a block the 4 A-rows are 4 gathered routed rows and the 4
+// B-columns are 4 output columns.  So one step advances 16 outputs of every
+// slice at once, and one wavefront holding a (4R rows) x (4C columns) tile
+// issues R*C steps per k element of its slices.
 //
-// Tile jobs are numbered expert-major (bucket e, column tile nt, row tile
-// mt), with the row tile fastest so the jobs that share an expert's weight
-// columns run together; every block walks the numbering with a grid stride.
-// The job count comes from the map's per-expert counts, which each block
-// reads and scans itself.  The last bucket (ids >= n_experts) gets quiet NaN
-// rows.
+// Block = WAVES wavefronts side by side along n: tile BM = 4R rows by
+// BN = 4C*WAVES columns.  Per round (128 k):
+//   * the gathered activation tile [BM][128] f32 goes through LDS, double
+//     buffered (the next round is loaded into registers while this one is
+//     computed, then written to the other buffer); 16-byte chunks are
+//     XOR-swizzled by row so the per-lane reads spread over the banks;
+//   * each wavefront reads its own weight columns straight from global memory
+//     into a two-round register ring (no reuse across wavefronts, so no LDS).
+// The 16 slice sums of each output are combined by a recursive-halving
+// exchange that keeps the canonical pairing (b with b^8, then b^4, b^2,
+// b^1) and leaves each lane with R*C/4 finished outputs.
+//
+// Jobs are numbered expert-major (bucket e, column tile nt, row tile mt), row
+// tile fastest; the block ids are remapped so that the blocks resident on
+// one XCD (the hardware deals blocks to the 8 XCDs round-robin) walk a
+// contiguous range of jobs and share that expert's weight columns in their
+// L2.  Each block reads the map's per-expert counts and scans them itself.
+// The last bucket (ids >= n_experts) gets quiet NaN rows.
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
+
+#ifndef EIDM_GROUPED_R
+#define EIDM_GROUPED_R 8
+#endif
+#ifndef EIDM_GROUPED_C
+#define EIDM_GROUPED_C 2
+#endif
+#ifndef EIDM_GROUPED_WAVES
+#define EIDM_GROUPED_WAVES 8
+#endif
 
 namespace eidm {
 namespace {
 
-constexpr int kGroupedThreads = 256;
+constexpr int kXcds = 8;
 
-template <int DT, int R, int C>
-__global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
-                                                                  const uint32_t* __restrict__ counts,
-                                                                  const uint32_t* __restrict__ offsets,
-                                                                  const uint32_t* __restrict__ rows) {
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Pieces { static constexpr int value = DtypeSize<DT>::value / 2; };
+
+// 16-byte chunk swizzle of the activation tile: row r's chunk c is stored at
+// chunk c ^ {0, 1, 8, 9}[r & 3] (rows are 32 chunks = 512 bytes), so the 16
+// lanes (4 slices x 4 rows) of one read touch 16 different chunk columns.
+__device__ __forceinline__ int swz(int row, int chunk) {
+    const int t = row & 3;
+    return chunk ^ ((t & 1) | ((t & 2) << 2));  // 0, 1, 8, 9
+}
+
+template <int DT>
+__device__ __forceinline__ void load_w_pieces(const uint8_t* row, int kk, u32x4 (&p)[Pieces<DT>::value]) {
     constexpr int S = DtypeSize<DT>::value;
-    constexpr int BM = 8 * R, BN = 8 * C;  // 2x2 wavefronts of (4R x 4C)
-    extern __shared__ uint32_t job_start[];  // [buckets + 1]
-    __shared__ uint32_t wave_tot[4];
+#pragma unroll
+    for (int i = 0; i < Pieces<DT>::value; ++i)
+        p[i] = *(reinterpret_cast<const u32x4*>(row + (size_t)kk * S) + i);
+}
+
+template <int DT>
+__device__ __forceinline__ void widen_w_pieces(const u32x4 (&p)[Pieces<DT>::value], float (&w)[kGranule]) {
+    if constexpr (DT == kDtypeF32) {
+        w[0] = __uint_as_float(p[0].x); w[1] = __uint_as_float(p[0].y);
+        w[2] = __uint_as_float(p[0].z); w[3] = __uint_as_float(p[0].w);
+        w[4] = __uint_as_float(p[1].x); w[5] = __uint_as_float(p[1].y);
+        w[6] = __uint_as_float(p[1].z); w[7] = __uint_as_float(p[1].w);
+    } else {
+        widen_pair<DT>(p[0].x, w[0], w[1]);
+        widen_pair<DT>(p[0].y, w[2], w[3]);
+        widen_pair<DT>(p[0].z, w[4], w[5]);
+        widen_pair<DT>(p[0].w, w[6], w[7]);
+    }
+}
+
+// One round's weight granules for this lane's C columns (whole 16-byte
+// granules of a vector round).
+template <int DT, int C>
+struct WeightRound {
+    u32x4 p[C][Pieces<DT>::value];
+};
+
+// This thread's share of one round's activation tile.
+template <int N>
+struct XTile {
+    f32x4 v[N];
+};
+
+template <int DT, int C>
+__device__ __forceinline__ void widen_w_pieces_all(const WeightRound<DT, C>& wr, float (&w)[C][kGranule]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) widen_w_pieces<DT>(wr.p[c], w[c]);
+}
+
+template <int DT, int R, int C, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
+                                                                const uint32_t* __restrict__ counts,
+                                                                const uint32_t* __restrict__ offsets,
+                                                                const uint32_t* __restrict__ rows) {
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int BM = 4 * R, BN = 4 * C * WAVES;
+    constexpr int XCHUNKS = BM * (kRoundK / 4);          // 16-byte chunks per activation tile
+    static_assert(XCHUNKS % THREADS == 0, "activation tile must split evenly");
+    constexpr int XPER = XCHUNKS / THREADS;              // chunks per thread per round
+    constexpr int NP = Pieces<DT>::value;
+
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* xs = reinterpret_cast<float*>(smem);          // [2][BM][128]
+    uint32_t* job_start = reinterpret_cast<uint32_t*>(smem + 2 * BM * kRoundK * sizeof(float));
+    __shared__ uint32_t wave_tot[WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = lane >> 2, q = lane & 3;
-    const int wr = wave >> 1, wc = wave & 1;
     const uint32_t buckets = a.n_experts + 1;
     const uint32_t ntiles = (a.n + BN - 1) / BN;
     const int n = (int)a.n, k = (int)a.k;
 
     // jobs per bucket -> exclusive prefix in LDS
     {
-        const uint32_t per = (buckets + kGroupedThreads - 1) / kGroupedThreads;
+        const uint32_t per = (buckets + THREADS - 1) / THREADS;
         const uint32_t begin = min(buckets, (uint32_t)tid * per);
         const uint32_t end = min(buckets, begin + per);
         uint32_t s = 0;
@@ -66,7 +148,7 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
         if (lane == 63) wave_tot[wave] = inc;
         __syncthreads();
         uint32_t run = inc - s, total = 0;
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < WAVES; ++w) {
             if (w < wave) run += wave_tot[w];
             total += wave_tot[w];
         }
@@ -80,11 +162,13 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
     }
     const uint32_t total_jobs = job_start[buckets];
     const int rounds = (k + kRoundK - 1) / kRoundK;
-    const bool vec = a.vec;
+    const int full = a.vec ? k / kRoundK : 0;  // vector rounds (whole aligned granules)
+    // XCD-contiguous job walk (the grid is a multiple of 8 blocks)
+    const uint32_t per_xcd = gridDim.x / kXcds;
+    const uint32_t vblock = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
 
-    for (uint32_t job = blockIdx.x; job < total_jobs; job += gridDim.x) {
-        // bucket of this job: last e with job_start[e] <= job
-        uint32_t lo = 0, hi = buckets;  // invariant: job_start[lo] <= job < job_start[hi]
+    for (uint32_t job = vblock; job < total_jobs; job += gridDim.x) {
+        uint32_t lo = 0, hi = buckets;  // job_start[lo] <= job < job_start[hi]
         while (hi - lo > 1) {
             const uint32_t mid = (lo + hi) >> 1;
             if (job_start[mid] <= job) lo = mid; else hi = mid;
@@ -95,33 +179,62 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
         const uint32_t nt = local / mtiles, mt = local % mtiles;
         const uint32_t row_begin = offsets[e] + mt * BM;
         const int row_count = (int)min((uint32_t)BM, counts[e] - mt * BM);
-        const int col_base = (int)(nt * BN) + wc * 4 * C;
-        const int row_base = wr * 4 * R;  // within the tile
+        const int col_base = (int)(nt * BN) + wave * 4 * C;
 
         if (e == a.n_experts) {  // ids naming no expert: NaN rows
-            for (int i = lane; i < 4 * R * 4 * C; i += 64) {
-                const int lr = row_base + i / (4 * C), col = col_base + i % (4 * C);
+            for (int i = tid; i < BM * BN; i += THREADS) {
+                const int lr = i / BN, col = (int)(nt * BN) + i % BN;
                 if (lr < row_count && col < n)
                     a.output[(size_t)rows[row_begin + lr] * a.n + col] = quiet_nan();
             }
             continue;
         }
 
-        // A operand rows: lane q feeds row 4r+q of each row group r
-        const float* xrow[R];
-        bool rvalid[R];
+        // ---- activation staging: this thread's XPER chunks (rows tid/32 + j*THREADS/32)
+        const float* xsrc[XPER];
+        bool xvalid[XPER];
+        int xrow_l[XPER], xchunk[XPER];
+        // rows past row_count read the tile's first row: their outputs are
+        // never stored, and the loads stay branch-free
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int lr = row_base + 4 * r + q;
-            rvalid[r] = lr < row_count;
-            uint32_t xr = 0;
-            if (rvalid[r]) {
-                const uint32_t rho = rows[row_begin + lr];
-                xr = a.layout == 1 ? rho : rho / a.top_k;
-            }
-            xrow[r] = a.input + (size_t)xr * a.k;
+        for (int j = 0; j < XPER; ++j) {
+            const int id = tid + j * THREADS;
+            xrow_l[j] = id >> 5;
+            xchunk[j] = id & 31;
+            xvalid[j] = xrow_l[j] < row_count;
+            const uint32_t rho = rows[row_begin + (xvalid[j] ? xrow_l[j] : 0)];
+            const uint32_t xr = a.layout == 1 ? rho : rho / a.top_k;
+            xsrc[j] = a.input + (size_t)xr * a.k + xchunk[j] * 4;
         }
-        // B operand columns: lane q feeds column 4c+q of each column group c
+        // whole 16-byte chunks of a vector round (every lane, no masks)
+        auto load_x_vec = [&](int g) {
+            XTile<XPER> t;
+#pragma unroll
+            for (int j = 0; j < XPER; ++j) t.v[j] = *reinterpret_cast<const f32x4*>(xsrc[j] + g * kRoundK);
+            return t;
+        };
+        // masked chunks: zero past k (the k tail) and for rows past row_count
+        auto load_x_masked = [&](int g) {
+            XTile<XPER> t;
+#pragma unroll
+            for (int j = 0; j < XPER; ++j) {
+                const int kk = g * kRoundK + xchunk[j] * 4;
+                const float* p = xsrc[j] + g * kRoundK;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t.v[j][i] = xvalid[j] && kk + i < k ? p[i] : 0.0f;
+            }
+            return t;
+        };
+        auto load_x = [&](int g) { return g < full ? load_x_vec(g) : load_x_masked(g); };
+        auto store_x = [&](int buf, const XTile<XPER>& t) {
+#pragma unroll
+            for (int j = 0; j < XPER; ++j) {
+                float* dst = xs + ((size_t)buf * BM + xrow_l[j]) * kRoundK + swz(xrow_l[j], xchunk[j]) * 4;
+                *reinterpret_cast<f32x4*>(dst) = t.v[j];
+            }
+        };
+
+        // ---- this lane's weight columns
         const uint8_t* wexp = static_cast<const uint8_t*>(a.weights) + (size_t)e * a.stride;
         const uint8_t* wrow[C];
         bool cvalid[C];
@@ -129,8 +242,25 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
         for (int c = 0; c < C; ++c) {
             const int col = col_base + 4 * c + q;
             cvalid[c] = col < n;
-            wrow[c] = wexp + (size_t)(cvalid[c] ? col : 0) * a.k * S;
+            wrow[c] = wexp + (size_t)(cvalid[c] ? col : 0) * a.k * DtypeSize<DT>::value;
         }
+        auto fetch_w_vec = [&](int g, WeightRound<DT, C>& wr) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) load_w_pieces<DT>(wrow[c], g * kRoundK + b * kGranule, wr.p[c]);
+        };
+        auto fetch_w = [&](int g, WeightRound<DT, C>& wr) {
+            if (g < full) fetch_w_vec(g, wr);
+        };
+        auto widen_w = [&](int g, const WeightRound<DT, C>& wr, float (&w)[C][kGranule]) {
+            if (g < full) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) widen_w_pieces<DT>(wr.p[c], w[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+                    load_weight_granule<DT>(wrow[c], g * kRoundK + b * kGranule, k, cvalid[c], a.vec, w[c]);
+            }
+        };
 
         f32x4 acc[R][C];
 #pragma unroll
@@ -138,65 +268,144 @@ __global__ __launch_bounds__(kGroupedThreads) void grouped_kernel(MatmulArgs a,
 #pragma unroll
             for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int g = 0; g < rounds; ++g) {
-            const int kk = g * kRoundK + b * kGranule;
-            float x[R][kGranule];
-            float w[C][kGranule];
+        // one round from LDS buffer `buf`: k elements in pairs (8-byte reads),
+        // each pair feeding R*C accumulation steps per element
+        auto compute = [&](int buf, const float (&w)[C][kGranule]) {
+            const float* xb = xs + (size_t)buf * BM * kRoundK;
 #pragma unroll
-            for (int r = 0; r < R; ++r) load_input_granule(xrow[r], kk, k, rvalid[r], vec, x[r]);
+            for (int pr = 0; pr < 4; ++pr) {
+                float2 xa[R];
 #pragma unroll
-            for (int c = 0; c < C; ++c) load_weight_granule<DT>(wrow[c], kk, k, cvalid[c], vec, w[c]);
+                for (int r = 0; r < R; ++r) {
+                    const int row = 4 * r + q;
+                    const int chunk = swz(row, 2 * b + (pr >> 1));
+                    xa[r] = *reinterpret_cast<const float2*>(xb + row * kRoundK + chunk * 4 + (pr & 1) * 2);
+                }
 #pragma unroll
-            for (int i = 0; i < kGranule; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < R; ++r)
+                    for (int r = 0; r < R; ++r) {
+                        const float xv = i == 0 ? xa[r].x : xa[r].y;
 #pragma unroll
-                    for (int c = 0; c < C; ++c) acc[r][c] = mfma_step(x[r][i], w[c][i], acc[r][c]);
+                        for (int c = 0; c < C; ++c)
+                            acc[r][c] = mfma_step(xv, w[c][2 * pr + i], acc[r][c]);
+                    }
+            }
+        };
+
+        // ---- software pipeline over rounds.  Load order per round: the
+        // next round's activations, then the weights two rounds ahead, so the
+        // wait for the activations (before their LDS store) never waits for
+        // the younger weight loads.
+        WeightRound<DT, C> ring[2];
+        {
+            const XTile<XPER> t = load_x(0);
+            fetch_w(0, ring[0]);
+            fetch_w(1, ring[1]);
+            __syncthreads();  // the previous job is done with both buffers
+            store_x(0, t);
+        }
+        __syncthreads();
+        int g = 0;
+        // steady state: vector rounds with both refills, no branches
+        for (; g + 4 <= full; g += 2) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const int gg = g + d;
+                const XTile<XPER> t = load_x_vec(gg + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                float w[C][kGranule];
+                widen_w_pieces_all<DT, C>(ring[d], w);
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_w_vec(gg + 2, ring[d]);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(d, w);
+                __builtin_amdgcn_sched_barrier(0);
+                store_x(d ^ 1, t);
+                __syncthreads();
+            }
+        }
+        // the remaining rounds (k tail, unaligned rows, short k)
+        for (; g < rounds; g += 2) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const int gg = g + d;
+                if (gg < rounds) {
+                    const bool more = gg + 1 < rounds;
+                    XTile<XPER> t{};
+                    if (more) t = load_x(gg + 1);
+                    float w[C][kGranule];
+                    widen_w(gg, ring[d], w);
+                    fetch_w(gg + 2, ring[d]);
+                    compute(d, w);
+                    if (more) store_x(d ^ 1, t);
+                    __syncthreads();
+                }
+            }
         }
 
-        // slice totals; lanes of slice b < 4 write output row 4r+b, column 4c+q
-        uint32_t out_row[R];
-        bool out_valid[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int lr = row_base + 4 * r + (b & 3);
-            out_valid[r] = b < 4 && lr < row_count;
-            out_row[r] = out_valid[r] ? rows[row_begin + lr] : 0;
-        }
+        // ---- slice sums: recursive halving over lane bits 5, 4, 3, 2
+        // value index o = (r*C + c)*4 + v; after the exchange lane (b, q)
+        // holds o = PER*b + j, j < PER.
+        constexpr int NV = R * C * 4;
+        constexpr int PER = NV / 16;
+        static_assert(NV % 16 == 0, "the exchange halves the values four times");
+        float val[NV];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                float t[4];
+            for (int c = 0; c < C; ++c)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) t[v] = slice_tree(acc[r][c][v]);
-                const float mine = b == 0 ? t[0] : b == 1 ? t[1] : b == 2 ? t[2] : t[3];
-                const int col = col_base + 4 * c + q;
-                if (out_valid[r] && col < n) a.output[(size_t)out_row[r] * a.n + col] = mine;
+                for (int v = 0; v < 4; ++v) val[(r * C + c) * 4 + v] = acc[r][c][v];
+#pragma unroll
+        for (int level = 0; level < 4; ++level) {
+            const int mask = 32 >> level;       // lane bit exchanged
+            const int half = NV >> (level + 1); // values kept after this level
+            const bool upper = (lane & mask) != 0;
+#pragma unroll
+            for (int j = 0; j < half; ++j) {
+                const float mine = upper ? val[half + j] : val[j];
+                const float other = upper ? val[j] : val[half + j];
+                val[j] = mine + __shfl_xor(other, mask);
             }
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int o = PER * b + j;
+            const int r = o / (4 * C), c = (o / 4) % C, v = o % 4;
+            const int lr = 4 * r + v;
+            const int col = col_base + 4 * c + q;
+            if (lr < row_count && col < n)
+                a.output[(size_t)rows[row_begin + lr] * a.n + col] = val[j];
+        }
     }
 }
 
-template <int DT, int R, int C>
+template <int DT, int R, int C, int WAVES>
 hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                       hipStream_t stream) {
-    constexpr uint32_t BM = 8 * R, BN = 8 * C;
+    constexpr uint32_t BM = 4 * R, BN = 4 * C * WAVES;
     const uint64_t routed = (uint64_t)a.m * a.top_k;
     const uint64_t ntiles = (a.n + BN - 1) / BN;
     // every bucket adds at most one partial row tile
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
-    const uint64_t resident = (uint64_t)(device_cus > 0 ? device_cus : 256) * 2;
-    const uint32_t grid = (uint32_t)(job_bound < resident ? job_bound : resident);
-    const size_t lds = (a.n_experts + 2) * sizeof(uint32_t);
-    hipLaunchKernelGGL((grouped_kernel<DT, R, C>), dim3(grid), dim3(kGroupedThreads), lds, stream,
-                       a, buf.counts, buf.offsets, buf.rows);
+    const size_t lds = 2 * BM * kRoundK * sizeof(float) + (a.n_experts + 2) * sizeof(uint32_t);
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_kernel<DT, R, C, WAVES>,
+                                                     64 * WAVES, lds) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const uint64_t resident = (uint64_t)(device_cus > 0 ? device_cus : 256) * per_cu;
+    uint64_t grid = job_bound < resident ? job_bound : resident;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((grouped_kernel<DT, R, C, WAVES>), dim3((uint32_t)grid), dim3(64 * WAVES), lds,
+                       stream, a, buf.counts, buf.offsets, buf.rows);
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_dt(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                      hipStream_t stream) {
-    return launch_cfg<DT, 4, 4>(a, buf, device_cus, stream);
+    return launch_cfg<DT, EIDM_GROUPED_R, EIDM_GROUPED_C, EIDM_GROUPED_WAVES>(a, buf, device_cus, stream);
 }
 
 }  // namespace

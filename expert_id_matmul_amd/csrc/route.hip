@@ -18,18 +18,46 @@
 namespace eidm {
 namespace {
 
-constexpr uint32_t kNone = 0xffffffffu;
+// Monotone map of an f32 key to u32: larger key -> larger code, -0 as +0, a
+// NaN below every number.
+__device__ __forceinline__ uint32_t order_code(float f) {
+    if (f != f) return 0u;
+    if (f == 0.0f) f = 0.0f;
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-// Strict total order on (key, index): larger key first, a NaN key after
-// every number, equal keys (and NaN pairs) by lower index.  An empty slot
-// (index kNone) ranks last.
-__device__ __forceinline__ bool ranks_before(float a, uint32_t ai, float b, uint32_t bi) {
-    if (ai == kNone) return false;
-    if (bi == kNone) return true;
-    const bool an = a != a, bn = b != b;
-    if (an != bn) return bn;
-    if (!an && a != b) return a > b;
-    return ai < bi;
+// 64-bit rank: code in the high word, (~index) in the low word, so the
+// maximum is the largest key with ties going to the lower index.  0 marks an
+// expert that is taken or does not exist.
+__device__ __forceinline__ uint64_t rank_of(float sel, uint32_t e) {
+    return ((uint64_t)order_code(sel) << 32) | (uint64_t)(0xffffffffu - e);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the wavefront: quad swaps, half-row and row mirrors (DPP), then
+// the four row maxima through scalar registers.
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
+    v = umax64(v, dpp64<0xb1>(v));   // quad_perm [1,0,3,2]
+    v = umax64(v, dpp64<0x4e>(v));   // quad_perm [2,3,0,1]
+    v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
+    v = umax64(v, dpp64<0x140>(v));  // row_mirror
+    return umax64(umax64(readlane64(v, 0), readlane64(v, 16)),
+                  umax64(readlane64(v, 32), readlane64(v, 48)));
 }
 
 template <int NV>
@@ -43,61 +71,47 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     if (t >= m) return;
     const float* lrow = logits + (size_t)t * n_experts;
 
-    float s[NV], sel[NV];
+    float s[NV];
+    uint64_t key[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const uint32_t e = (uint32_t)v * 64 + lane;
         s[v] = 0.0f;
-        sel[v] = 0.0f;
+        key[v] = 0;
         if (e < n_experts) {
-            const double sd = 1.0 / (1.0 + exp(-(double)lrow[e]));
-            s[v] = (float)sd;
-            sel[v] = s[v] + (bias ? bias[e] : 0.0f);
+            s[v] = (float)(1.0 / (1.0 + exp(-(double)lrow[e])));
+            const float sel = s[v] + (bias ? bias[e] : 0.0f);
+            key[v] = rank_of(sel, e);
         }
     }
 
-    uint32_t taken = 0;  // bit v: value v of this lane already picked
-    float gsum = 0.0f;
+    uint32_t my_id = 0;
+    float my_s = 0.0f, gsum = 0.0f;
     for (uint32_t j = 0; j < top_k; ++j) {
-        float bs = 0.0f;
-        uint32_t bi = kNone;
+        uint64_t best = 0;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const uint32_t e = (uint32_t)v * 64 + lane;
-            if (e < n_experts && !((taken >> v) & 1u) && ranks_before(sel[v], e, bs, bi)) {
-                bs = sel[v];
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float os = __shfl_xor(bs, off);
-            const uint32_t oi = __shfl_xor(bi, off);
-            if (ranks_before(os, oi, bs, bi)) {
-                bs = os;
-                bi = oi;
-            }
-        }
-        // every lane now holds the same winner
-        const int owner = (int)(bi & 63u);
-        const int slot = (int)(bi >> 6);
+        for (int v = 0; v < NV; ++v) best = umax64(best, key[v]);
+        best = wave_max(best);  // wave-uniform
+        const uint32_t e = 0xffffffffu - (uint32_t)best;
+        const int owner = (int)(e & 63u), slot = (int)(e >> 6);
         float mine = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-            if (v == slot) mine = s[v];
-        if (lane == owner) taken |= 1u << slot;
-        const float sw = __shfl(mine, owner);
-        if (lane == 0) {
-            ids[(size_t)t * top_k + j] = bi;
-            gsum += sw;
-            if (gates) gates[(size_t)t * top_k + j] = sw;
+        for (int v = 0; v < NV; ++v) {
+            if (v == slot) {
+                mine = s[v];
+                if (lane == owner) key[v] = 0;
+            }
+        }
+        const float sw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine), owner));
+        gsum += sw;  // slot order, identical in every lane
+        if (lane == (int)j) {
+            my_id = e;
+            my_s = sw;
         }
     }
-    if (lane == 0 && gates && renormalize) {
-        for (uint32_t j = 0; j < top_k; ++j) {
-            float* g = gates + (size_t)t * top_k + j;
-            *g = __fdiv_rn(*g, gsum);
-        }
+    if (lane < (int)top_k) {
+        ids[(size_t)t * top_k + lane] = my_id;
+        if (gates) gates[(size_t)t * top_k + lane] = renormalize ? __fdiv_rn(my_s, gsum) : my_s;
     }
 }
 

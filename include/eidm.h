@@ -152,7 +152,8 @@ int eidm_query(const eidm_shape* shape, int route, eidm_requirements* out);
  *              order) when renormalize != 0, else s[t,ids[t,j]]
  * logits: device f32 [m, n_experts]; bias: device f32 [n_experts] or NULL;
  * ids: device u32 [m, top_k]; gates: device f32 [m, top_k] (may be NULL).
- * Requires 1 <= top_k <= n_experts <= 2048.  Logits must be finite (a NaN
+ * Requires 1 <= top_k <= min(n_experts, 64) and n_experts <= 2048 (larger
+ * values return EIDM_E_UNSUPPORTED).  Logits must be finite (a NaN
  * logit ranks below every finite one; the ids stay distinct and in range).
  */
 int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,

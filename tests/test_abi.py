@@ -132,6 +132,7 @@ def test_route_map_combine_reject_bad_arguments(lib):
     assert L.eidm_route_topk(None, None, 4, 8, 2, 1, P(FAKE), None, None) == B.E_INVALID
     assert L.eidm_route_topk(P(FAKE), None, 4, 4096, 2, 1, P(FAKE), None, None) == B.E_UNSUPPORTED
     assert L.eidm_route_topk(P(FAKE + 2), None, 4, 8, 2, 1, P(FAKE), None, None) == B.E_ALIGN
+    assert L.eidm_route_topk(P(FAKE), None, 4, 128, 65, 1, P(FAKE), None, None) == B.E_UNSUPPORTED
     assert L.eidm_combine(0, 2, 8, P(FAKE), P(FAKE), P(FAKE), None) == B.E_INVALID
     assert L.eidm_combine(2, 2, 8, None, P(FAKE), P(FAKE), None) == B.E_INVALID
     assert L.eidm_combine(2, 2, 8, P(FAKE + 1), P(FAKE), P(FAKE), None) == B.E_ALIGN
