@@ -28,13 +28,16 @@
 #include "eidm_internal.hpp"
 
 #ifndef EIDM_DIRECT_C
-#define EIDM_DIRECT_C 1
+#define EIDM_DIRECT_C 2
 #endif
 #ifndef EIDM_DIRECT_WAVES
-#define EIDM_DIRECT_WAVES 4
+#define EIDM_DIRECT_WAVES 2
 #endif
 #ifndef EIDM_DIRECT_DEPTH
-#define EIDM_DIRECT_DEPTH 8
+#define EIDM_DIRECT_DEPTH 6
+#endif
+#ifndef EIDM_DIRECT_NT
+#define EIDM_DIRECT_NT 1
 #endif
 
 namespace eidm {
@@ -112,8 +115,14 @@ __global__ __launch_bounds__(64 * WAVES) void direct_kernel(MatmulArgs a) {
         for (int c = 0; c < C; ++c)
 #pragma unroll
             for (int i = 0; i < NP; ++i)
-                s.w[c][i] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(wrow[c] + (size_t)g * kRoundK * S) + i);
+            {
+                const u32x4* p = reinterpret_cast<const u32x4*>(wrow[c] + (size_t)g * kRoundK * S) + i;
+#if EIDM_DIRECT_NT
+                s.w[c][i] = __builtin_nontemporal_load(p);  // weights are read once per call
+#else
+                s.w[c][i] = *p;
+#endif
+            }
         s.x[0] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK);
         s.x[1] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK + 4);
     };
