@@ -55,6 +55,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int DT> struct Pieces { static constexpr int value = DtypeSize<DT>::value / 2; };
 
+template <int V> struct IntC { static constexpr int value = V; };
+
 // 16-byte chunk swizzle of the activation tile: row r's chunk c is stored at
 // chunk c ^ {0, 1, 8, 9}[r & 3] (rows are 32 chunks = 512 bytes), so the 16
 // lanes (4 slices x 4 rows) of one read touch 16 different chunk columns.
@@ -381,6 +383,291 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
     }
 }
 
+// Streamed form, for k an even number of whole vector rounds: the
+// rounds of all the jobs one block walks are a single stream.  The loads of a
+// job's first rounds are issued while the previous job computes its last
+// ones, the next job's row indices are fetched a whole job ahead, and the
+// job table (bucket counts, offsets, first job) sits in LDS, so a block never
+// waits on a dependent chain of global reads between jobs.  Arithmetic and
+// order are those of grouped_kernel.
+template <int DT, int R, int C, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
+                                                                       const uint32_t* __restrict__ counts,
+                                                                       const uint32_t* __restrict__ offsets,
+                                                                       const uint32_t* __restrict__ rows) {
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int BM = 4 * R, BN = 4 * C * WAVES;
+    constexpr int XCHUNKS = BM * (kRoundK / 4);
+    static_assert(XCHUNKS % THREADS == 0, "activation tile must split evenly");
+    constexpr int XPER = XCHUNKS / THREADS;
+    constexpr int S = DtypeSize<DT>::value;
+    constexpr int NV = R * C * 4;
+    constexpr int PER = NV / 16;
+    static_assert(NV % 16 == 0, "the exchange halves the values four times");
+
+    const uint32_t buckets = a.n_experts + 1;
+    extern __shared__ __align__(16) uint8_t smem[];
+    float* xs = reinterpret_cast<float*>(smem);          // [2][BM][128]
+    uint32_t* job_start = reinterpret_cast<uint32_t*>(smem + 2 * BM * kRoundK * sizeof(float));
+    uint32_t* cnt_s = job_start + buckets + 1;            // [buckets]
+    uint32_t* off_s = cnt_s + buckets;                    // [buckets]
+    __shared__ uint32_t wave_tot[WAVES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = lane >> 2, q = lane & 3;
+    const uint32_t ntiles = (a.n + BN - 1) / BN;
+    const int n = (int)a.n, k = (int)a.k;
+    const int rounds = k / kRoundK;
+
+    // job table: jobs per bucket -> exclusive prefix, with counts and offsets
+    {
+        const uint32_t per = (buckets + THREADS - 1) / THREADS;
+        const uint32_t begin = min(buckets, (uint32_t)tid * per);
+        const uint32_t end = min(buckets, begin + per);
+        uint32_t s = 0;
+        for (uint32_t i = begin; i < end; ++i) {
+            const uint32_t c = counts[i];
+            cnt_s[i] = c;
+            off_s[i] = offsets[i];
+            const uint32_t jobs = ((c + BM - 1) / BM) * ntiles;
+            job_start[i] = jobs;
+            s += jobs;
+        }
+        uint32_t inc = s;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(inc, d);
+            if (lane >= d) inc += o;
+        }
+        if (lane == 63) wave_tot[wave] = inc;
+        __syncthreads();
+        uint32_t run = inc - s, total = 0;
+        for (int w = 0; w < WAVES; ++w) {
+            if (w < wave) run += wave_tot[w];
+            total += wave_tot[w];
+        }
+        for (uint32_t i = begin; i < end; ++i) {
+            const uint32_t v = job_start[i];
+            job_start[i] = run;
+            run += v;
+        }
+        if (tid == 0) job_start[buckets] = total;
+        __syncthreads();
+    }
+    const uint32_t total_jobs = job_start[buckets];
+    const uint32_t per_xcd = gridDim.x / kXcds;
+    uint32_t job = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (job >= total_jobs) return;  // the whole block leaves together
+
+    struct Job {
+        uint32_t e;          // bucket (n_experts = ids naming no expert)
+        uint32_t wexp;       // expert whose weights are read (e, or 0 for that bucket)
+        uint32_t col0;       // first output column of the tile
+        uint32_t row_begin;  // first entry of the tile in the row map
+        int row_count;
+    };
+    auto decode = [&](uint32_t jb) {
+        uint32_t lo = 0, hi = buckets;  // job_start[lo] <= jb < job_start[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (job_start[mid] <= jb) lo = mid; else hi = mid;
+        }
+        Job j;
+        j.e = __builtin_amdgcn_readfirstlane(lo);
+        const uint32_t cnt = __builtin_amdgcn_readfirstlane(cnt_s[j.e]);
+        const uint32_t local = jb - __builtin_amdgcn_readfirstlane(job_start[j.e]);
+        const uint32_t mtiles = (cnt + BM - 1) / BM;
+        const uint32_t nt = local / mtiles, mt = local % mtiles;
+        j.wexp = j.e < a.n_experts ? j.e : 0;
+        j.col0 = nt * BN;
+        j.row_begin = __builtin_amdgcn_readfirstlane(off_s[j.e]) + mt * BM;
+        j.row_count = (int)min((uint32_t)BM, cnt - mt * BM);
+        return j;
+    };
+
+    // per-lane routed-row indices of a job (from the row map): the
+    // activation rows this thread stages and the rows of its finished
+    // outputs (rows past row_count read the tile's first row: never stored)
+    struct Rows {
+        uint32_t x[XPER];
+        uint32_t out[PER];
+    };
+    auto fetch_rows = [&](const Job& j) {
+        Rows g;
+#pragma unroll
+        for (int jj = 0; jj < XPER; ++jj) {
+            const int lr = (tid + jj * THREADS) >> 5;
+            g.x[jj] = rows[j.row_begin + (lr < j.row_count ? lr : 0)];
+        }
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int o = PER * b + p;
+            const int lr = 4 * (o / (4 * C)) + o % 4;
+            g.out[p] = rows[j.row_begin + (lr < j.row_count ? lr : 0)];
+        }
+        return g;
+    };
+
+    const uint32_t x_div = a.layout == 1 ? 1u : a.top_k;  // routed row -> activation row
+    auto load_x = [&](const uint32_t (&routed)[XPER], int g) {
+        XTile<XPER> t;
+#pragma unroll
+        for (int jj = 0; jj < XPER; ++jj) {
+            const int chunk = (tid + jj * THREADS) & 31;
+            const uint32_t xr = routed[jj] / x_div;
+            t.v[jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + g * kRoundK + chunk * 4);
+        }
+        return t;
+    };
+    auto store_x = [&](int buf, const XTile<XPER>& t) {
+#pragma unroll
+        for (int jj = 0; jj < XPER; ++jj) {
+            const int id = tid + jj * THREADS;
+            const int lr = id >> 5, chunk = id & 31;
+            float* dst = xs + ((size_t)buf * BM + lr) * kRoundK + swz(lr, chunk) * 4;
+            *reinterpret_cast<f32x4*>(dst) = t.v[jj];
+        }
+    };
+    // this lane's weight granules of round g (columns past n read column n-1)
+    auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
+        const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)j.wexp * a.stride;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int col = min((int)j.col0 + wave * 4 * C + 4 * c + q, n - 1);
+            load_w_pieces<DT>(base + (size_t)col * a.k * S, g * kRoundK + b * kGranule, wr.p[c]);
+        }
+    };
+
+    f32x4 acc[R][C];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf, const float (&w)[C][kGranule]) {
+        const float* xb = xs + (size_t)buf * BM * kRoundK;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            float2 xa[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = 4 * r + q;
+                const int chunk = swz(row, 2 * b + (pr >> 1));
+                xa[r] = *reinterpret_cast<const float2*>(xb + row * kRoundK + chunk * 4 + (pr & 1) * 2);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float xv = i == 0 ? xa[r].x : xa[r].y;
+#pragma unroll
+                    for (int c = 0; c < C; ++c) acc[r][c] = mfma_step(xv, w[c][2 * pr + i], acc[r][c]);
+                }
+        }
+    };
+
+    // slice sums (recursive halving over lane bits 5, 4, 3, 2, as in
+    // grouped_kernel) and the stores of one finished job
+    auto finish = [&](const Job& j, const Rows& g) {
+        float val[NV];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) val[(r * C + c) * 4 + v] = acc[r][c][v];
+#pragma unroll
+        for (int level = 0; level < 4; ++level) {
+            const int mask = 32 >> level;
+            const int half = NV >> (level + 1);
+            const bool upper = (lane & mask) != 0;
+#pragma unroll
+            for (int jj = 0; jj < half; ++jj) {
+                const float mine = upper ? val[half + jj] : val[jj];
+                const float other = upper ? val[jj] : val[half + jj];
+                val[jj] = mine + __shfl_xor(other, mask);
+            }
+        }
+        const bool nan_rows = j.e == a.n_experts;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int o = PER * b + p;
+            const int r = o / (4 * C), c = (o / 4) % C, v = o % 4;
+            const int lr = 4 * r + v;
+            const int col = (int)j.col0 + wave * 4 * C + 4 * c + q;
+            if (lr < j.row_count && col < n)
+                a.output[(size_t)g.out[p] * a.n + col] = nan_rows ? quiet_nan() : val[p];
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    // Two job slots, used alternately (static indices: loads in flight are
+    // never copied between registers): while slot c's job runs, slot 1-c
+    // holds the next job, whose row indices are already in flight.  The
+    // block's job count is known up front, so the job loop has one exit.
+    const uint32_t my_jobs = (total_jobs - job + gridDim.x - 1) / gridDim.x;
+    Job jobs[2];
+    Rows rws[2];
+    uint32_t next = job + gridDim.x;
+    jobs[0] = decode(job);
+    rws[0] = fetch_rows(jobs[0]);
+    jobs[1] = next < total_jobs ? decode(next) : jobs[0];
+    rws[1] = fetch_rows(jobs[1]);
+
+    WeightRound<DT, C> ring[2];  // even rounds in slot 0, odd in slot 1
+    {
+        const XTile<XPER> t = load_x(rws[0].x, 0);
+        fetch_w(jobs[0], 0, ring[0]);
+        fetch_w(jobs[0], 1, ring[1]);
+        store_x(0, t);
+    }
+    __syncthreads();
+
+    // One round: load the activations of the round after it (this job's, or
+    // the next job's first), widen this round's weights and refill their
+    // slot two rounds ahead, compute, publish the activations.
+    auto step = [&](auto dc, const uint32_t (&xrows)[XPER], int gx, const Job& wj, int gw) {
+        constexpr int d = decltype(dc)::value;
+        const XTile<XPER> t = load_x(xrows, gx);
+        __builtin_amdgcn_sched_barrier(0);
+        float w[C][kGranule];
+        widen_w_pieces_all<DT, C>(ring[d], w);
+        __builtin_amdgcn_sched_barrier(0);
+        fetch_w(wj, gw, ring[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(d, w);
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(d ^ 1, t);
+        __syncthreads();
+    };
+    // the job in slot c (rounds is even: round g uses slot and buffer g & 1);
+    // afterwards slot c takes the job after next (or repeats slot 1-c's
+    // job when there is none: its loads stay in bounds, its results unused)
+    auto run_job = [&](auto cc) {
+        constexpr int c = decltype(cc)::value, o = 1 - c;
+        int g = 0;
+        for (; g + 2 < rounds; g += 2) {
+            step(IntC<0>{}, rws[c].x, g + 1, jobs[c], g + 2);
+            step(IntC<1>{}, rws[c].x, g + 2, jobs[c], g + 3);
+        }
+        step(IntC<0>{}, rws[c].x, g + 1, jobs[o], 0);
+        step(IntC<1>{}, rws[o].x, 0, jobs[o], 1);
+        finish(jobs[c], rws[c]);
+        next += gridDim.x;
+        jobs[c] = next < total_jobs ? decode(next) : jobs[o];
+        rws[c] = fetch_rows(jobs[c]);
+    };
+    uint32_t i = 0;
+    for (; i + 2 <= my_jobs; i += 2) {
+        run_job(IntC<0>{});
+        run_job(IntC<1>{});
+    }
+    if (i < my_jobs) run_job(IntC<0>{});
+}
+
 template <int DT, int R, int C, int WAVES>
 hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                       hipStream_t stream) {
@@ -389,16 +676,20 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const uint64_t ntiles = (a.n + BN - 1) / BN;
     // every bucket adds at most one partial row tile
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
-    const size_t lds = 2 * BM * kRoundK * sizeof(float) + (a.n_experts + 2) * sizeof(uint32_t);
+    // the streamed form needs an even number of whole vector rounds
+    const bool stream_form = a.vec && a.k % (2 * kRoundK) == 0;
+    auto kernel = stream_form ? grouped_stream_kernel<DT, R, C, WAVES> : grouped_kernel<DT, R, C, WAVES>;
+    const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4) : (a.n_experts + 2);
+    const size_t lds = 2 * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_kernel<DT, R, C, WAVES>,
-                                                     64 * WAVES, lds) != hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * WAVES, lds) != hipSuccess ||
+        per_cu < 1)
         per_cu = 1;
     const uint64_t resident = (uint64_t)(device_cus > 0 ? device_cus : 256) * per_cu;
     uint64_t grid = job_bound < resident ? job_bound : resident;
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    hipLaunchKernelGGL((grouped_kernel<DT, R, C, WAVES>), dim3((uint32_t)grid), dim3(64 * WAVES), lds,
-                       stream, a, buf.counts, buf.offsets, buf.rows);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(64 * WAVES), lds, stream, a, buf.counts,
+                       buf.offsets, buf.rows);
     return hipGetLastError();
 }
 

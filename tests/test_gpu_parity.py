@@ -58,6 +58,12 @@ SMALL = [
     _wl("one_expert_top1", W.DT_F16, 17, 40, 96, 1, 1, seed=35),
     _wl("m1_decode_like", W.DT_BF16, 1, 136, 1024, 8, 64, seed=36),
     _wl("may_repeat", W.DT_BF16, 12, 48, 256, 5, 3, mult=W.IDS_MAY_REPEAT, seed=37, ids_kind="repeat"),
+    # k an even number of whole 128-element rounds: Grouped streams the rounds
+    # of consecutive jobs; these give blocks several jobs each, in odd and
+    # even numbers, with a ragged last column tile
+    _wl("stream_bf16_jobs", W.DT_BF16, 256, 1000, 512, 8, 16, seed=60),
+    _wl("stream_f16_slot", W.DT_F16, 150, 700, 256, 6, 10, layout=W.LAYOUT_SLOTTED, seed=61),
+    _wl("stream_f32", W.DT_F32, 128, 2000, 256, 4, 8, seed=62),
 ]
 
 
@@ -132,8 +138,10 @@ def test_modular_fill_weights(lib):
     assert_close(yd, _oracle_y(wl, wb, x, ids))
 
 
-def test_ids_naming_no_expert_give_nan_rows_in_both_routes(lib):
-    wl = _wl("bad_ids", W.DT_BF16, 10, 40, 200, 3, 6, seed=50)
+@pytest.mark.parametrize("m,n,k", [(10, 40, 200), (200, 640, 512)], ids=["masked", "streamed"])
+def test_ids_naming_no_expert_give_nan_rows_in_both_routes(lib, m, n, k):
+    print(f"[case] bad ids m={m} n={n} k={k}", flush=True)
+    wl = _wl("bad_ids", W.DT_BF16, m, n, k, 3, 6, seed=50)
     wb = W.weight_bytes(wl)
     x = W.activations(wl)
     ids = W.ids(wl).copy()
