@@ -37,10 +37,10 @@
 #include "eidm_internal.hpp"
 
 #ifndef EIDM_GROUPED_R
-#define EIDM_GROUPED_R 8
+#define EIDM_GROUPED_R 4
 #endif
 #ifndef EIDM_GROUPED_C
-#define EIDM_GROUPED_C 2
+#define EIDM_GROUPED_C 4
 #endif
 #ifndef EIDM_GROUPED_WAVES
 #define EIDM_GROUPED_WAVES 8
@@ -617,44 +617,51 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     jobs[1] = next < total_jobs ? decode(next) : jobs[0];
     rws[1] = fetch_rows(jobs[1]);
 
-    WeightRound<DT, C> ring[2];  // even rounds in slot 0, odd in slot 1
+    // Register rings two rounds deep, slot = round parity: the weights of
+    // rounds g and g+1, and the activations of round g+1 (published to LDS
+    // at the end of round g) and g+2.
+    WeightRound<DT, C> ring[2];
+    XTile<XPER> xring[2];
     {
         const XTile<XPER> t = load_x(rws[0].x, 0);
+        xring[1] = load_x(rws[0].x, 1);
         fetch_w(jobs[0], 0, ring[0]);
         fetch_w(jobs[0], 1, ring[1]);
         store_x(0, t);
     }
     __syncthreads();
 
-    // One round: load the activations of the round after it (this job's, or
-    // the next job's first), widen this round's weights and refill their
-    // slot two rounds ahead, compute, publish the activations.
-    auto step = [&](auto dc, const uint32_t (&xrows)[XPER], int gx, const Job& wj, int gw) {
+    // One round (slot d): request the activations and weights two rounds
+    // ahead (this job's, or the next job's first two) into slot d, after
+    // widening this round's weights out of it; compute; publish the next
+    // round's activations.
+    auto step = [&](auto dc, const uint32_t (&xrows)[XPER], const Job& j, int g2) {
         constexpr int d = decltype(dc)::value;
-        const XTile<XPER> t = load_x(xrows, gx);
+        xring[d] = load_x(xrows, g2);
         __builtin_amdgcn_sched_barrier(0);
         float w[C][kGranule];
         widen_w_pieces_all<DT, C>(ring[d], w);
         __builtin_amdgcn_sched_barrier(0);
-        fetch_w(wj, gw, ring[d]);
+        fetch_w(j, g2, ring[d]);
         __builtin_amdgcn_sched_barrier(0);
         compute(d, w);
         __builtin_amdgcn_sched_barrier(0);
-        store_x(d ^ 1, t);
+        store_x(d ^ 1, xring[d ^ 1]);
         __syncthreads();
     };
-    // the job in slot c (rounds is even: round g uses slot and buffer g & 1);
-    // afterwards slot c takes the job after next (or repeats slot 1-c's
-    // job when there is none: its loads stay in bounds, its results unused)
+    // the job in slot c (rounds is even: round g uses slots and buffer
+    // g & 1); afterwards slot c takes the job after next (or repeats slot
+    // 1-c's job when there is none: its loads stay in bounds, its results
+    // unused)
     auto run_job = [&](auto cc) {
         constexpr int c = decltype(cc)::value, o = 1 - c;
         int g = 0;
         for (; g + 2 < rounds; g += 2) {
-            step(IntC<0>{}, rws[c].x, g + 1, jobs[c], g + 2);
-            step(IntC<1>{}, rws[c].x, g + 2, jobs[c], g + 3);
+            step(IntC<0>{}, rws[c].x, jobs[c], g + 2);
+            step(IntC<1>{}, rws[c].x, jobs[c], g + 3);
         }
-        step(IntC<0>{}, rws[c].x, g + 1, jobs[o], 0);
-        step(IntC<1>{}, rws[o].x, 0, jobs[o], 1);
+        step(IntC<0>{}, rws[o].x, jobs[o], 0);
+        step(IntC<1>{}, rws[o].x, jobs[o], 1);
         finish(jobs[c], rws[c]);
         next += gridDim.x;
         jobs[c] = next < total_jobs ? decode(next) : jobs[o];
@@ -693,10 +700,17 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     return hipGetLastError();
 }
 
+// Tile shape per weight type.  16-bit weights: BM = 16 rows x BN = 128
+// columns (small row tiles waste few rows in an expert's last tile); f32
+// weights need twice the registers per weight round, so they take R = 8,
+// C = 2 (32 x 64 tiles) to stay within 256 VGPRs.
 template <int DT>
 hipError_t launch_dt(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                      hipStream_t stream) {
-    return launch_cfg<DT, EIDM_GROUPED_R, EIDM_GROUPED_C, EIDM_GROUPED_WAVES>(a, buf, device_cus, stream);
+    if constexpr (DT == kDtypeF32)
+        return launch_cfg<DT, 8, 2, 8>(a, buf, device_cus, stream);
+    else
+        return launch_cfg<DT, EIDM_GROUPED_R, EIDM_GROUPED_C, EIDM_GROUPED_WAVES>(a, buf, device_cus, stream);
 }
 
 }  // namespace
