@@ -13,10 +13,11 @@ Cache.  The prefill configurations (m=2048 down projection with per-slot
 input; m=512 balanced and maximally skewed) are reported next to it in
 TFLOP/s.
 
-Steps are captured once into a HIP graph and replayed (the CPU cost of
-launching would otherwise exceed a decode step); per-kernel durations come
-from HIP events around each matmul call in an eager pass of the same steps,
-recorded on the stream the kernels run on.
+A decode step is one launch of the fused kernel (route, Direct matmul and
+combine); 32 steps are captured into a HIP graph and replayed, and HIP
+events on the replaying stream bracket the timed replays, so the per-step
+time is that kernel's average launch duration.  The prefill matmul calls
+are timed one by one with HIP events on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -127,6 +128,18 @@ def kernel_times(call, steps: int, before=None, after=None):
 
 
 # ---------------------------------------------------------------------- decode
+def decode_bytes(wl) -> dict:
+    """Algorithmic HBM bytes of one decode step: the touched experts' weights
+    (top_k distinct experts, n*k each) plus every other input and output once."""
+    touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
+    other = (wl.m * wl.k * 4                  # x
+             + wl.m * wl.n_experts * 4 + wl.n_experts * 4   # logits, bias
+             + wl.routed_rows * wl.n * 4      # y
+             + wl.m * wl.n * 4                # out
+             + wl.routed_rows * 8)            # ids, gates
+    return {"touched_weights": touched, "algorithmic": touched + other}
+
+
 def bench_decode(lib, steps: int, warmup: int):
     wl = W.WORKLOADS["decode"]
     shape = B.shape_of(wl)
@@ -151,40 +164,38 @@ def bench_decode(lib, steps: int, warmup: int):
     y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
     out = torch.empty((wl.m, wl.n), dtype=torch.float32, device="cuda")
 
-    def route(i):
-        lib.route_topk(logits_d[i % ROT][None], bias_d[i % ROT], wl.top_k, ids, gates)
-
-    def matmul(i):
-        lib.matmul_id(shape, B.DIRECT, weights, x, ids, y, weight_bytes=wl.weight_bytes)
-
-    def combine(i):
-        lib.combine(y, gates, out)
-
     def step(i):
-        route(i)
-        matmul(i)
-        combine(i)
+        # route -> Direct matmul -> combine: one fused kernel
+        lib.moe_forward(shape, B.DIRECT, weights, x, logits_d[i % ROT][None], bias_d[i % ROT], ids, gates,
+                        y, out, None, weight_bytes=wl.weight_bytes)
+
+    def step_unfused(i):
+        lib.route_topk(logits_d[i % ROT][None], bias_d[i % ROT], wl.top_k, ids, gates)
+        lib.matmul_id(shape, B.DIRECT, weights, x, ids, y, weight_bytes=wl.weight_bytes)
+        lib.combine(y, gates, out)
 
     timed = Timed(step, ROT)
     res = timed.run(steps, warmup)
-    # the graph's last step against the same step run eagerly
-    graph_out = out.clone()
-    graph_ids = ids.clone()
+    # the graph's last step against the same step run eagerly, and against
+    # the three separate calls
+    graph_out, graph_ids = out.clone(), ids.clone()
     step(ROT - 1)
     torch.cuda.synchronize()
     assert torch.equal(graph_out, out) and torch.equal(graph_ids, ids), "graph replay differs from eager"
     assert sorted(graph_ids.cpu().numpy()[0].tolist()) == list(range(8 * (ROT - 1), 8 * ROT))
-    # per-kernel: the Direct kernel alone, eager, between the same route/combine launches
-    direct_ms = kernel_times(matmul, max(ROT, steps), before=route, after=combine)
-    touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
-    med = _percentiles(direct_ms)["median"]
-    avg = float(np.mean(direct_ms))
+    step_unfused(ROT - 1)
+    torch.cuda.synchronize()
+    assert torch.equal(graph_out.view(torch.int32), out.view(torch.int32)), "fused and unfused steps differ"
+    unfused = Timed(step_unfused, ROT).run(max(ROT, steps // 4), max(ROT, warmup // 4))
+    nbytes = decode_bytes(wl)
+    t = res["gpu_ms_per_step"] * 1e-3
     res.update({
-        "touched_bytes": touched,
-        "value_gbs": touched / (res["gpu_ms_per_step"] * 1e-3) / 1e9,
-        "direct_ms": {"avg": avg, **_percentiles(direct_ms), "n": len(direct_ms)},
-        "direct_gbs": touched / (avg * 1e-3) / 1e9,
-        "direct_gbs_median": touched / (med * 1e-3) / 1e9,
+        "kernel": "moe_direct_kernel (route + Direct matmul + combine, one launch per step)",
+        "touched_bytes": nbytes["touched_weights"],
+        "algorithmic_bytes": nbytes["algorithmic"],
+        "value_gbs": nbytes["touched_weights"] / t / 1e9,
+        "algorithmic_gbs": nbytes["algorithmic"] / t / 1e9,
+        "unfused_ms_per_step": unfused["gpu_ms_per_step"],
     })
     del weights
     torch.cuda.empty_cache()
@@ -221,8 +232,9 @@ def bench_prefill(lib, name: str, steps: int, warmup: int):
         lib.combine(y, gates, out)
 
     timed = Timed(step, 4)
-    res = timed.run(max(4, steps // 4), max(4, warmup // 4) if warmup else 0)
-    mm = kernel_times(matmul, max(8, steps // 4))
+    # prefill steps are ~40x longer than decode steps: fewer of them
+    res = timed.run(max(16, steps // 16), max(8, warmup // 64) if warmup else 0)
+    mm = kernel_times(matmul, max(16, steps // 32))
     flops = 2.0 * wl.routed_rows * wl.n * wl.k
     avg = float(np.mean(mm))
     res.update({
@@ -237,6 +249,40 @@ def bench_prefill(lib, name: str, steps: int, warmup: int):
     del weights
     torch.cuda.empty_cache()
     return res
+
+
+# ---------------------------------------------------------------------- counters
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_direct_kernel_decode_hbm_counters.txt")
+DECODE_SOURCES = ("moe_direct.hip", "direct_wave.hpp", "route_wave.hpp", "eidm_device.hpp",
+                  "eidm_internal.hpp")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "expert_id_matmul_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    """HBM bytes per launch of the fused decode kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the same counters on
+    a copy of known size; None when that summary is missing or was taken on
+    other kernel sources than the ones built now."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if ":" in ln:
+                    k, v = ln.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("sources_sha256") != decode_source_hash():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------- CPU oracle
@@ -275,29 +321,57 @@ def cpu_baseline(budget_s: float = 15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=64)
+    # the clocks take a few hundred milliseconds of load to ramp up: the
+    # default warm-up is about half a second of decode steps
+    ap.add_argument("--steps", type=int, default=4096)
+    ap.add_argument("--warmup", type=int, default=16384)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="prefill configurations only (the line then has no headline value)")
+    ap.add_argument("--prefill", default="down_proj,prefill_balanced,prefill_skewed",
+                    help="comma-separated prefill configurations to run")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB five times (the known-size "
+                         "kernel that scales HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the expert-ID matmul path here has no multi-GPU "
               "form (sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+        return
     lib = B.load()
-    print(f"[bench] decode: {args.steps} steps, warmup {args.warmup}", file=sys.stderr, flush=True)
-    dec = bench_decode(lib, args.steps, args.warmup)
+    dec = None
+    if not args.no_decode:
+        print(f"[bench] decode: {args.steps} steps, warmup {args.warmup}", file=sys.stderr, flush=True)
+        dec = bench_decode(lib, args.steps, args.warmup)
     prefill = {}
     if not args.no_prefill:
-        for name in ("down_proj", "prefill_balanced", "prefill_skewed"):
+        for name in [p for p in args.prefill.split(",") if p]:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             prefill[name] = bench_prefill(lib, name, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline()
-    d = dec["direct_ms"]["avg"] * 1e-3
+    prefill_out = {k: {"tflops_step": round(v["tflops"], 2),
+                       "tflops_matmul": round(v["grouped_tflops"], 2),
+                       "frac_f32_peak_matmul": round(v["grouped_tflops"] * 1e12 / F32_PEAK, 4),
+                       "ms_per_step": round(v["gpu_ms_per_step"], 4),
+                       "matmul_ms": v["grouped_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
+                   for k, v in prefill.items()}
+    if dec is None:
+        print(json.dumps({"prefill": prefill_out}), flush=True)
+        return
     line = {
         "metric": "expert-ID matmul: decode weight GB/s (m=1) + prefill TFLOP/s (m=2048) at 1 GPU",
         "value": round(dec["value_gbs"], 2),
@@ -314,17 +388,12 @@ def main():
         "config": {"workload": "decode: m=1 k=4096 n=1536 n_experts=256 top_k=8, bf16 weights, "
                                "f32 activations, sigmoid+bias routing, cold experts",
                    "weights": "bf16", "m": 1, "n": 1536, "k": 4096, "n_experts": 256, "top_k": 8},
-        "roofline": {"kernel": "direct_kernel<bf16>", "bound": "hbm",
-                     "achieved": round(dec["touched_bytes"] / d / 1e9, 1), "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": round(dec["touched_bytes"] / d / HBM_PEAK, 4),
-                     "traffic": None},
+        "roofline": {"kernel": "moe_direct_kernel<bf16> (fused decode step)", "bound": "hbm",
+                     "achieved": round(dec["algorithmic_gbs"], 1), "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": round(dec["algorithmic_gbs"] * 1e9 / HBM_PEAK, 4),
+                     "traffic": decode_traffic()},
         "decode_detail": dec,
-        "prefill": {k: {"tflops_step": round(v["tflops"], 2),
-                        "tflops_matmul": round(v["grouped_tflops"], 2),
-                        "frac_f32_peak_matmul": round(v["grouped_tflops"] * 1e12 / F32_PEAK, 4),
-                        "ms_per_step": round(v["gpu_ms_per_step"], 4),
-                        "matmul_ms": v["grouped_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
-                    for k, v in prefill.items()},
+        "prefill": prefill_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

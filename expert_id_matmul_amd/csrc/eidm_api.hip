@@ -374,6 +374,13 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
     rc = check_combine_args(shape->m, shape->top_k, shape->n, y, gates, out);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (chosen == EIDM_ROUTE_DIRECT && eidm::moe_direct_supported(shape->top_k, shape->n_experts)) {
+        // one kernel: route, Direct matmul and combine per (token, column group)
+        const hipError_t err = eidm::launch_moe_direct(args, logits, bias, renormalize, ids, gates, out, device_cus(), st);
+        if (err != hipSuccess) return device_fail(err, "fused route/Direct/combine launch");
+        if (route_taken) *route_taken = chosen;
+        return ok();
+    }
     hipError_t err = eidm::launch_route(logits, bias, shape->m, shape->n_experts, shape->top_k,
                                         renormalize, ids, gates, st);
     if (err != hipSuccess) return device_fail(err, "route launch");

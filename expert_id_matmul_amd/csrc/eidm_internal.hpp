@@ -11,6 +11,8 @@ constexpr uint32_t kMaxExperts = 2048;
 
 // Largest top_k the router takes (one pick per lane).
 constexpr uint32_t kMaxRouterTopK = 64;
+// fused route -> Direct -> combine: one wavefront per slot in a block
+constexpr uint32_t kMaxMoeDirectTopK = 16;
 
 struct MatmulArgs {
     int dtype;
@@ -46,5 +48,9 @@ hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device
                           hipStream_t stream);
 hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,
                           const float* gates, float* out, hipStream_t stream);
+bool moe_direct_supported(uint32_t top_k, uint32_t n_experts);
+// a.ids is ignored: the kernel writes the picks to `ids` and reads them itself
+hipError_t launch_moe_direct(const MatmulArgs& a, const float* logits, const float* bias, int renormalize,
+                             uint32_t* ids, float* gates, float* out, int device_cus, hipStream_t stream);
 
 }  // namespace eidm

@@ -225,6 +225,10 @@ int eidm_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const f
  * [n_experts] or NULL; ids/gates/y/out are caller buffers that receive the
  * intermediate and final results.  shape->id_multiplicity must be
  * DISTINCT_PER_TOKEN (the router's ids are distinct).
+ * When the route taken is Direct and top_k <= 16, the three steps run as
+ * one kernel (per token and column group: route, Direct product of every
+ * slot, combine) with the same results bit for bit as the three separate
+ * calls; ids, gates and y are still written.
  */
 int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights,
                      uint64_t weight_bytes, const float* input, const float* logits,

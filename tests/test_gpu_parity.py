@@ -287,3 +287,49 @@ def test_moe_forward_small_down_projection(lib, route):
     assert np.array_equal(u32(ids), ids_o)
     assert_close(y.cpu().numpy(), y_o, what="y")
     assert_close(check_guarded(out, wl.m * wl.n).reshape(wl.m, wl.n), out_o, what="out")
+
+
+@pytest.mark.parametrize("dtype,m,n,k,top_k,n_experts,layout", [
+    (W.DT_BF16, 3, 200, 1000, 8, 256, W.LAYOUT_SHARED),    # decode-like, ragged n, k tail
+    (W.DT_F32, 2, 37, 64, 5, 300, W.LAYOUT_SLOTTED),       # > 256 experts, k below one round
+    (W.DT_F16, 4, 64, 256, 16, 64, W.LAYOUT_SHARED),       # 16 slots per token
+    (W.DT_BF16, 5, 48, 384, 1, 7, W.LAYOUT_SLOTTED),       # one slot
+], ids=["bf16_decode_like", "f32_many_experts", "f16_top16", "bf16_top1"])
+def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k, top_k, n_experts, layout):
+    """With the Direct route the whole path runs as one kernel; its ids, gates,
+    y and out must be the bits of route_topk -> matmul_id -> combine."""
+    print(f"[case] fused moe_forward dtype={dtype} m={m} n={n} k={k} top_k={top_k} E={n_experts}", flush=True)
+    wl = _wl("fused", dtype, m, n, k, top_k, n_experts, layout=layout, seed=70 + top_k)
+    wl = wl.with_(ids_kind="logits")
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    logits = W.router_logits(wl)
+    bias = W.router_bias(wl)
+    shape = B.shape_of(wl)
+    wdev = to_dev(wb)
+
+    def bufs():
+        return (torch.empty((m, top_k), dtype=torch.int32, device="cuda"),
+                torch.empty((m, top_k), dtype=torch.float32, device="cuda"),
+                poisoned_output(wl.routed_rows * n), poisoned_output(m * n))
+
+    ids_f, gates_f, y_f, out_f = bufs()
+    taken = lib.moe_forward(shape, B.DIRECT, wdev, to_dev(x), to_dev(logits), to_dev(bias), ids_f, gates_f,
+                            y_f, out_f, None, weight_bytes=wl.weight_bytes)
+    assert taken == B.DIRECT
+    ids_s, gates_s, y_s, out_s = bufs()
+    lib.route_topk(to_dev(logits), to_dev(bias), top_k, ids_s, gates_s)
+    lib.matmul_id(shape, B.DIRECT, wdev, to_dev(x), ids_s, y_s, None, weight_bytes=wl.weight_bytes)
+    lib.combine(y_s[:wl.routed_rows * n].view(wl.routed_rows, n), gates_s, out_s[:m * n].view(m, n))
+    torch.cuda.synchronize()
+    assert torch.equal(ids_f, ids_s)
+    assert torch.equal(gates_f.view(torch.int32), gates_s.view(torch.int32))
+    yf = check_guarded(y_f, wl.routed_rows * n)
+    assert np.array_equal(yf.view(np.uint32), check_guarded(y_s, wl.routed_rows * n).view(np.uint32))
+    of = check_guarded(out_f, m * n)
+    assert np.array_equal(of.view(np.uint32), check_guarded(out_s, m * n).view(np.uint32))
+    ids_o, gates_o, _, _ = oracle.route(logits, bias, top_k)
+    assert np.array_equal(u32(ids_f), ids_o)
+    y_o = _oracle_y(wl, wb, x, ids_o)
+    assert_close(yf.reshape(wl.routed_rows, n), y_o, what="fused y")
+    assert_close(of.reshape(m, n), oracle.combine(y_o, gates_o, top_k), what="fused out")
