@@ -56,6 +56,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <int DT> struct Pieces { static constexpr int value = DtypeSize<DT>::value / 2; };
 
 template <int V> struct IntC { static constexpr int value = V; };
+static_assert(EIDM_GROUPED_R == 4 || EIDM_GROUPED_R == 8, "row-group dispatch covers R = 4 and R = 8");
 
 // 16-byte chunk swizzle of the activation tile: row r's chunk c is stored at
 // chunk c ^ {0, 1, 8, 9}[r & 3] (rows are 32 chunks = 512 bytes), so the 16
@@ -407,8 +408,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
 
     const uint32_t buckets = a.n_experts + 1;
     extern __shared__ __align__(16) uint8_t smem[];
-    float* xs = reinterpret_cast<float*>(smem);          // [2][BM][128]
-    uint32_t* job_start = reinterpret_cast<uint32_t*>(smem + 2 * BM * kRoundK * sizeof(float));
+    float* xs = reinterpret_cast<float*>(smem);          // [2 buffers][2 rounds][BM][128]
+    uint32_t* job_start = reinterpret_cast<uint32_t*>(smem + 4 * BM * kRoundK * sizeof(float));
     uint32_t* cnt_s = job_start + buckets + 1;            // [buckets]
     uint32_t* off_s = cnt_s + buckets;                    // [buckets]
     __shared__ uint32_t wave_tot[WAVES];
@@ -509,24 +510,30 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     };
 
     const uint32_t x_div = a.layout == 1 ? 1u : a.top_k;  // routed row -> activation row
+    // this thread's chunks of the activation tiles of rounds g and g+1
     auto load_x = [&](const uint32_t (&routed)[XPER], int g) {
-        XTile<XPER> t;
+        XTile<2 * XPER> t;
 #pragma unroll
-        for (int jj = 0; jj < XPER; ++jj) {
-            const int chunk = (tid + jj * THREADS) & 31;
-            const uint32_t xr = routed[jj] / x_div;
-            t.v[jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + g * kRoundK + chunk * 4);
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int jj = 0; jj < XPER; ++jj) {
+                const int chunk = (tid + jj * THREADS) & 31;
+                const uint32_t xr = routed[jj] / x_div;
+                t.v[h * XPER + jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + (g + h) * kRoundK + chunk * 4);
+            }
         return t;
     };
-    auto store_x = [&](int buf, const XTile<XPER>& t) {
+    // publish them to LDS buffer `buf` (rounds in halves 0 and 1)
+    auto store_x = [&](int buf, const XTile<2 * XPER>& t) {
 #pragma unroll
-        for (int jj = 0; jj < XPER; ++jj) {
-            const int id = tid + jj * THREADS;
-            const int lr = id >> 5, chunk = id & 31;
-            float* dst = xs + ((size_t)buf * BM + lr) * kRoundK + swz(lr, chunk) * 4;
-            *reinterpret_cast<f32x4*>(dst) = t.v[jj];
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int jj = 0; jj < XPER; ++jj) {
+                const int id = tid + jj * THREADS;
+                const int lr = id >> 5, chunk = id & 31;
+                float* dst = xs + ((size_t)(2 * buf + h) * BM + lr) * kRoundK + swz(lr, chunk) * 4;
+                *reinterpret_cast<f32x4*>(dst) = t.v[h * XPER + jj];
+            }
     };
     // this lane's weight granules of round g (columns past n read column n-1)
     auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
@@ -544,13 +551,16 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
 #pragma unroll
         for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](int buf, const float (&w)[C][kGranule]) {
-        const float* xb = xs + (size_t)buf * BM * kRoundK;
+    // one round from LDS tile `tile` (= 2*buffer + half) for the first RR
+    // row groups of the tile
+    auto compute_rows = [&](int tile, const float (&w)[C][kGranule], auto rr) __attribute__((always_inline)) {
+        constexpr int RR = decltype(rr)::value;
+        const float* xb = xs + (size_t)tile * BM * kRoundK;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            float2 xa[R];
+            float2 xa[RR];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
+            for (int r = 0; r < RR; ++r) {
                 const int row = 4 * r + q;
                 const int chunk = swz(row, 2 * b + (pr >> 1));
                 xa[r] = *reinterpret_cast<const float2*>(xb + row * kRoundK + chunk * 4 + (pr & 1) * 2);
@@ -558,13 +568,14 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
+                for (int r = 0; r < RR; ++r) {
                     const float xv = i == 0 ? xa[r].x : xa[r].y;
 #pragma unroll
                     for (int c = 0; c < C; ++c) acc[r][c] = mfma_step(xv, w[c][2 * pr + i], acc[r][c]);
                 }
         }
     };
+
 
     // slice sums (recursive halving over lane bits 5, 4, 3, 2, as in
     // grouped_kernel) and the stores of one finished job
@@ -617,51 +628,58 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     jobs[1] = next < total_jobs ? decode(next) : jobs[0];
     rws[1] = fetch_rows(jobs[1]);
 
-    // Register rings two rounds deep, slot = round parity: the weights of
-    // rounds g and g+1, and the activations of round g+1 (published to LDS
-    // at the end of round g) and g+2.
+    // A step is two rounds: the weights of its rounds sit in register slots
+    // 0 and 1, its activations in one LDS buffer (two rounds), so one
+    // barrier serves two rounds.  During a step the next step's
+    // activations and weights are requested.
     WeightRound<DT, C> ring[2];
-    XTile<XPER> xring[2];
+    int buf = 0;
     {
-        const XTile<XPER> t = load_x(rws[0].x, 0);
-        xring[1] = load_x(rws[0].x, 1);
+        const XTile<2 * XPER> t = load_x(rws[0].x, 0);
         fetch_w(jobs[0], 0, ring[0]);
         fetch_w(jobs[0], 1, ring[1]);
         store_x(0, t);
     }
     __syncthreads();
 
-    // One round (slot d): request the activations and weights two rounds
-    // ahead (this job's, or the next job's first two) into slot d, after
-    // widening this round's weights out of it; compute; publish the next
-    // round's activations.
-    auto step = [&](auto dc, const uint32_t (&xrows)[XPER], const Job& j, int g2) {
-        constexpr int d = decltype(dc)::value;
-        xring[d] = load_x(xrows, g2);
+    // One step from LDS buffer `buf`: request the next step's activations
+    // (rounds gx, gx+1 of the rows xrows), then per round widen its weights,
+    // refill the slot with round gw (gw+1) of job j and compute; publish the
+    // activations to the other buffer.
+    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, auto rr) __attribute__((always_inline)) {
+        const XTile<2 * XPER> t = load_x(xrows, gx);
         __builtin_amdgcn_sched_barrier(0);
-        float w[C][kGranule];
-        widen_w_pieces_all<DT, C>(ring[d], w);
-        __builtin_amdgcn_sched_barrier(0);
-        fetch_w(j, g2, ring[d]);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(d, w);
-        __builtin_amdgcn_sched_barrier(0);
-        store_x(d ^ 1, xring[d ^ 1]);
-        __syncthreads();
-    };
-    // the job in slot c (rounds is even: round g uses slots and buffer
-    // g & 1); afterwards slot c takes the job after next (or repeats slot
-    // 1-c's job when there is none: its loads stay in bounds, its results
-    // unused)
-    auto run_job = [&](auto cc) {
-        constexpr int c = decltype(cc)::value, o = 1 - c;
-        int g = 0;
-        for (; g + 2 < rounds; g += 2) {
-            step(IntC<0>{}, rws[c].x, jobs[c], g + 2);
-            step(IntC<1>{}, rws[c].x, jobs[c], g + 3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float w[C][kGranule];
+            widen_w_pieces_all<DT, C>(ring[h], w);
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_w(j, gw + h, ring[h]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_rows(2 * buf + h, w, rr);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        step(IntC<0>{}, rws[o].x, jobs[o], 0);
-        step(IntC<1>{}, rws[o].x, jobs[o], 1);
+        store_x(buf ^ 1, t);
+        __syncthreads();
+        buf ^= 1;
+    };
+    // the job in slot c (rounds is even); afterwards slot c takes the job
+    // after next (or repeats slot 1-c's job when there is none: its loads
+    // stay in bounds, its results unused)
+    auto run_job = [&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value, o = 1 - c;
+        // An expert's last row tile skips the steps of its empty 4-row
+        // groups (their outputs are never stored; the others keep their
+        // order): the job runs with RR = R, R/2 or R/4 row groups.
+        auto steps = [&](auto rr) __attribute__((always_inline)) {
+            int g = 0;
+            for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, rr);
+            step(rws[o].x, 0, jobs[o], 0, rr);
+        };
+        const int groups = (jobs[c].row_count + 3) / 4;
+        if (groups > R / 2) steps(IntC<R>{});
+        else if (groups > R / 4) steps(IntC<R / 2>{});
+        else steps(IntC<R / 4>{});
         finish(jobs[c], rws[c]);
         next += gridDim.x;
         jobs[c] = next < total_jobs ? decode(next) : jobs[o];
@@ -687,7 +705,7 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const bool stream_form = a.vec && a.k % (2 * kRoundK) == 0;
     auto kernel = stream_form ? grouped_stream_kernel<DT, R, C, WAVES> : grouped_kernel<DT, R, C, WAVES>;
     const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4) : (a.n_experts + 2);
-    const size_t lds = 2 * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
+    const size_t lds = (stream_form ? 4 : 2) * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * WAVES, lds) != hipSuccess ||
         per_cu < 1)
