@@ -19,10 +19,11 @@ F32, F16, BF16 = 0, 1, 2
 SHARED_PER_TOKEN, SLOTTED = 0, 1
 DISTINCT_PER_TOKEN, MAY_REPEAT = 0, 1
 AUTO, DIRECT, GROUPED = 0, 1, 2
-OK, E_INVALID, E_UNSUPPORTED, E_SIZE, E_ALIGN, E_DEVICE = 0, -1, -2, -3, -4, -5
+OK, E_INVALID, E_UNSUPPORTED, E_SIZE, E_ALIGN, E_DEVICE, E_IDS = 0, -1, -2, -3, -4, -5, -6
 
 EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk", "eidm_map",
-           "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward"]
+           "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward",
+           "eidm_validate_ids"]
 
 
 class Shape(ctypes.Structure):
@@ -120,6 +121,8 @@ class Library:
                                      ctypes.POINTER(ctypes.c_int)]
         L.eidm_combine.restype = i32
         L.eidm_combine.argtypes = [u32, u32, u32, P, P, P, P]
+        L.eidm_validate_ids.restype = i32
+        L.eidm_validate_ids.argtypes = [P, u32, u32, u32, i32, ctypes.POINTER(ctypes.c_int32), P]
         L.eidm_moe_forward.restype = i32
         L.eidm_moe_forward.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, i32, P, P, P, P,
                                        P, u64, P, ctypes.POINTER(ctypes.c_int)]
@@ -216,6 +219,17 @@ class Library:
                                               _ptr(out), _ptr(scratch), sbytes, _stream(stream),
                                               ctypes.byref(taken)))
         return taken.value
+
+    def validate_ids(self, ids, n_experts: int, multiplicity: int = 0, stream=None) -> int:
+        """The smallest bad routed index of ids [m, top_k], or -1 (synchronous)."""
+        m, top_k = ids.shape
+        _need("ids", ids, m * top_k)
+        bad = ctypes.c_int32(-2)
+        rc = self.lib.eidm_validate_ids(_ptr(ids), m, top_k, n_experts, multiplicity, ctypes.byref(bad),
+                                        _stream(stream))
+        if rc not in (OK, E_IDS):
+            self._check(rc)
+        return bad.value
 
 
 _LIB: Library | None = None

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -328,6 +329,32 @@ int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts
     hipError_t err = eidm::launch_map(ids, (uint32_t)routed, n_experts, buf,
                                       static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return device_fail(err, "map launch");
+    return ok();
+}
+
+int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
+                      int multiplicity, int32_t* bad_index_out, void* stream) {
+    static std::mutex serial;  // the kernel reports through one device word
+    if (!ids || !bad_index_out) return fail(EIDM_E_INVALID, "ids or bad_index_out is NULL");
+    if (!m || !top_k || !n_experts) return fail(EIDM_E_INVALID, "zero dimension");
+    if (multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN && multiplicity != EIDM_IDS_MAY_REPEAT)
+        return fail(EIDM_E_INVALID, "unknown id multiplicity %d", multiplicity);
+    uint64_t routed;
+    if (!mul_ok(m, top_k, &routed) || routed > kIndexLimit)
+        return fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
+    if (!aligned(ids, 4)) return fail(EIDM_E_ALIGN, "ids must be 4-byte aligned");
+    int first_bad = -1;
+    {
+        std::lock_guard<std::mutex> lock(serial);
+        const hipError_t err = eidm::run_validate(ids, m, top_k, n_experts,
+                                                  multiplicity == EIDM_IDS_DISTINCT_PER_TOKEN,
+                                                  static_cast<hipStream_t>(stream), &first_bad);
+        if (err != hipSuccess) return device_fail(err, "id validation");
+    }
+    *bad_index_out = first_bad;
+    if (first_bad >= 0)
+        return fail(EIDM_E_IDS, "ids[%d] (token %u, slot %u) names no expert or repeats an earlier slot",
+                    first_bad, (unsigned)(first_bad / top_k), (unsigned)(first_bad % top_k));
     return ok();
 }
 

@@ -49,6 +49,9 @@ hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device
 hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,
                           const float* gates, float* out, hipStream_t stream);
 bool moe_direct_supported(uint32_t top_k, uint32_t n_experts);
+// synchronous: waits for `stream`; *first_bad = smallest bad routed index or -1
+hipError_t run_validate(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts, int distinct,
+                        hipStream_t stream, int* first_bad);
 // a.ids is ignored: the kernel writes the picks to `ids` and reads them itself
 hipError_t launch_moe_direct(const MatmulArgs& a, const float* logits, const float* bias, int renormalize,
                              uint32_t* ids, float* gates, float* out, int device_cus, hipStream_t stream);

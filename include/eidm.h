@@ -87,7 +87,8 @@ typedef enum eidm_status {
     EIDM_E_UNSUPPORTED = -2, /* route not legal for the shape                    */
     EIDM_E_SIZE = -3,        /* weight extent or scratch too small              */
     EIDM_E_ALIGN = -4,       /* pointer or stride misaligned for its type        */
-    EIDM_E_DEVICE = -5       /* a HIP call failed                                */
+    EIDM_E_DEVICE = -5,      /* a HIP call failed                                */
+    EIDM_E_IDS = -6          /* eidm_validate_ids found a bad id                 */
 } eidm_status;
 
 /*
@@ -217,6 +218,24 @@ int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint
  */
 int eidm_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const float* gates,
                  float* out, void* stream);
+
+/*
+ * Device-side check of an id table before it is used (mlx-native
+ * dense_matmul_id_auto.rs: the shape key's id multiplicity,
+ * DenseMatmulIdMultiplicity; distinct-per-token profile ids in
+ * fn calibration_buffers).  An entry r = t*top_k + s is bad when
+ * ids[r] >= n_experts or, with EIDM_IDS_DISTINCT_PER_TOKEN, when it equals
+ * an earlier slot of token t.
+ * ids           device u32 [m, top_k]
+ * multiplicity  eidm_multiplicity of the table
+ * bad_index_out host int32*: the smallest bad r, or -1 when none
+ * Returns EIDM_OK when every entry is good and EIDM_E_IDS otherwise.
+ * Synchronous: it waits for `stream` (so it cannot be captured in a graph).
+ * Calls on one device share a device word: calls from several host threads
+ * at once are serialised inside the library.  Requires m*top_k < 2^31.
+ */
+int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
+                      int multiplicity, int32_t* bad_index_out, void* stream);
 
 /*
  * The whole path in one call: route (eidm_route_topk) -> matmul

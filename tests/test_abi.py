@@ -148,3 +148,16 @@ def test_moe_forward_requires_distinct_ids(lib):
     rc = lib.lib.eidm_moe_forward(ctypes.byref(s), B.DIRECT, P(FAKE), 596, P(FAKE), P(FAKE), None, 1,
                                   P(FAKE), P(FAKE), P(FAKE), P(FAKE), None, 0, None, None)
     assert rc == B.E_INVALID
+
+
+def test_validate_ids_rejects_bad_arguments_before_launch(lib):
+    L = lib.lib
+    P = ctypes.c_void_p
+    bad = ctypes.c_int32(7)
+    assert L.eidm_validate_ids(None, 4, 2, 8, 0, ctypes.byref(bad), None) == B.E_INVALID
+    assert L.eidm_validate_ids(P(FAKE), 4, 2, 8, 0, None, None) == B.E_INVALID
+    assert L.eidm_validate_ids(P(FAKE), 0, 2, 8, 0, ctypes.byref(bad), None) == B.E_INVALID
+    assert L.eidm_validate_ids(P(FAKE), 4, 2, 8, 5, ctypes.byref(bad), None) == B.E_INVALID
+    assert L.eidm_validate_ids(P(FAKE + 2), 4, 2, 8, 0, ctypes.byref(bad), None) == B.E_ALIGN
+    assert L.eidm_validate_ids(P(FAKE), 1 << 30, 4, 8, 0, ctypes.byref(bad), None) == B.E_UNSUPPORTED
+    assert bad.value == 7  # untouched on failure

@@ -333,3 +333,40 @@ def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k,
     y_o = _oracle_y(wl, wb, x, ids_o)
     assert_close(yf.reshape(wl.routed_rows, n), y_o, what="fused y")
     assert_close(of.reshape(m, n), oracle.combine(y_o, gates_o, top_k), what="fused out")
+
+
+# ------------------------------------------------------------------ id validation
+def _first_bad(ids: np.ndarray, n_experts: int, distinct: bool) -> int:
+    """Brute force: the smallest flat index whose id names no expert or repeats
+    an earlier slot of its token."""
+    m, top_k = ids.shape
+    for t in range(m):
+        for s in range(top_k):
+            if ids[t, s] >= n_experts or (distinct and ids[t, s] in ids[t, :s]):
+                return t * top_k + s
+    return -1
+
+
+@pytest.mark.parametrize("case", ["good", "out_of_range", "repeat", "repeat_allowed", "several", "max_id"])
+def test_validate_ids_finds_the_first_bad_entry(lib, case):
+    print(f"[case] validate ids {case}", flush=True)
+    rng = np.random.default_rng(90)
+    m, top_k, E = 300, 6, 40
+    ids = np.stack([rng.permutation(E)[:top_k] for _ in range(m)]).astype(np.uint32)
+    distinct = case != "repeat_allowed"
+    if case == "out_of_range":
+        ids[123, 4] = E
+    elif case in ("repeat", "repeat_allowed"):
+        ids[77, 5] = ids[77, 2]
+    elif case == "several":
+        ids[200, 1] = 0xFFFFFFFF
+        ids[150, 3] = ids[150, 0]
+        ids[299, 5] = E + 7
+    elif case == "max_id":
+        ids[0, 0] = E - 1
+        ids[0, 1:] = np.arange(top_k - 1)
+    want = _first_bad(ids, E, distinct)
+    got = lib.validate_ids(ids_to_dev(ids), E, 0 if distinct else 1)
+    assert got == want
+    if case in ("good", "repeat_allowed", "max_id"):
+        assert got == -1
