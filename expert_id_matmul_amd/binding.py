@@ -23,7 +23,9 @@ OK, E_INVALID, E_UNSUPPORTED, E_SIZE, E_ALIGN, E_DEVICE, E_IDS = 0, -1, -2, -3, 
 
 EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk", "eidm_map",
            "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward",
-           "eidm_validate_ids"]
+           "eidm_validate_ids", "eidm_plan_create", "eidm_plan_destroy", "eidm_plan_freeze",
+           "eidm_plan_route", "eidm_calibration_workspace_bytes", "eidm_calibrate",
+           "eidm_matmul_id_planned"]
 
 
 class Shape(ctypes.Structure):
@@ -40,6 +42,24 @@ class Requirements(ctypes.Structure):
                 ("ids_elements", ctypes.c_uint64), ("output_elements", ctypes.c_uint64),
                 ("scratch_bytes", ctypes.c_uint64), ("grouped_legal", ctypes.c_int32),
                 ("reserved0", ctypes.c_int32)]
+
+
+class Calibration(ctypes.Structure):
+    """eidm_calibration (include/eidm.h)."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("route", ctypes.c_int32),
+                ("grouped_legal", ctypes.c_int32), ("bit_identical", ctypes.c_int32),
+                ("reason", ctypes.c_int32), ("reserved0", ctypes.c_int32)] + [
+        (name, ctypes.c_double * 2) for name in (
+            "direct_wall_p25", "direct_wall_median", "direct_wall_p75", "direct_gpu_median",
+            "grouped_wall_p25", "grouped_wall_median", "grouped_wall_p75", "grouped_gpu_median")]
+
+    def as_dict(self) -> dict:
+        return {name: (list(getattr(self, name)) if isinstance(getattr(self, name), ctypes.Array)
+                       else getattr(self, name)) for name, _ in self._fields_}
+
+
+CAL_REASONS = ["grouped wins", "grouped not legal", "grouped failed", "not bit identical",
+               "wall median", "wall quartiles", "gpu median"]
 
 
 class EidmError(RuntimeError):
@@ -123,6 +143,21 @@ class Library:
         L.eidm_combine.argtypes = [u32, u32, u32, P, P, P, P]
         L.eidm_validate_ids.restype = i32
         L.eidm_validate_ids.argtypes = [P, u32, u32, u32, i32, ctypes.POINTER(ctypes.c_int32), P]
+        L.eidm_plan_create.restype = P
+        L.eidm_plan_create.argtypes = []
+        L.eidm_plan_destroy.restype = None
+        L.eidm_plan_destroy.argtypes = [P]
+        L.eidm_plan_freeze.restype = i32
+        L.eidm_plan_freeze.argtypes = [P]
+        L.eidm_plan_route.restype = i32
+        L.eidm_plan_route.argtypes = [P, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int)]
+        L.eidm_calibration_workspace_bytes.restype = u64
+        L.eidm_calibration_workspace_bytes.argtypes = [ctypes.POINTER(Shape)]
+        L.eidm_calibrate.restype = i32
+        L.eidm_calibrate.argtypes = [P, ctypes.POINTER(Shape), P, u64, P, u64, P, ctypes.POINTER(Calibration)]
+        L.eidm_matmul_id_planned.restype = i32
+        L.eidm_matmul_id_planned.argtypes = [P, ctypes.POINTER(Shape), P, u64, P, P, P, P, u64, P,
+                                             ctypes.POINTER(ctypes.c_int)]
         L.eidm_moe_forward.restype = i32
         L.eidm_moe_forward.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, i32, P, P, P, P,
                                        P, u64, P, ctypes.POINTER(ctypes.c_int)]
@@ -230,6 +265,60 @@ class Library:
         if rc not in (OK, E_IDS):
             self._check(rc)
         return bad.value
+
+
+class Plan:
+    """A route plan (eidm_plan): activation-time calibration of exact shapes,
+    then lookups; the plan is destroyed with this object."""
+
+    def __init__(self, lib: Library):
+        self.lib = lib
+        self.handle = lib.lib.eidm_plan_create()
+        if not self.handle:
+            raise MemoryError("eidm_plan_create")
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            self.lib.lib.eidm_plan_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+    def workspace_bytes(self, shape: Shape) -> int:
+        return self.lib.lib.eidm_calibration_workspace_bytes(ctypes.byref(shape))
+
+    def calibrate(self, shape: Shape, weights, workspace, weight_bytes: int | None = None,
+                  stream=None) -> Calibration:
+        if weight_bytes is None:
+            weight_bytes = _nbytes(weights)
+        _need("weights", weights, weight_bytes, 1)
+        _need("workspace", workspace, self.workspace_bytes(shape), 1)
+        rec = Calibration()
+        rec.struct_size = ctypes.sizeof(Calibration)
+        self.lib._check(self.lib.lib.eidm_calibrate(ctypes.c_void_p(self.handle), ctypes.byref(shape),
+                                                    _ptr(weights), weight_bytes, _ptr(workspace),
+                                                    _nbytes(workspace), _stream(stream), ctypes.byref(rec)))
+        return rec
+
+    def freeze(self) -> None:
+        self.lib._check(self.lib.lib.eidm_plan_freeze(ctypes.c_void_p(self.handle)))
+
+    def route(self, shape: Shape) -> int:
+        r = ctypes.c_int(-1)
+        self.lib._check(self.lib.lib.eidm_plan_route(ctypes.c_void_p(self.handle), ctypes.byref(shape),
+                                                     ctypes.byref(r)))
+        return r.value
+
+    def matmul_id(self, shape: Shape, weights, input, ids, output, scratch=None,
+                  weight_bytes: int | None = None, stream=None) -> int:
+        if weight_bytes is None:
+            weight_bytes = _nbytes(weights)
+        route = self.route(shape)
+        self.lib._check_matmul_buffers(shape, route, weights, weight_bytes, input, ids, output, scratch)
+        sbytes = _nbytes(scratch) if scratch is not None else 0
+        taken = ctypes.c_int(-1)
+        self.lib._check(self.lib.lib.eidm_matmul_id_planned(
+            ctypes.c_void_p(self.handle), ctypes.byref(shape), _ptr(weights), weight_bytes, _ptr(input),
+            _ptr(ids), _ptr(output), _ptr(scratch), sbytes, _stream(stream), ctypes.byref(taken)))
+        return taken.value
 
 
 _LIB: Library | None = None

@@ -1,0 +1,391 @@
+// calibrate.hip -- activation-time choice between the Direct and Grouped
+// forms for exact shapes, and the frozen plan that serves that choice.
+//
+// mlx-native 0.13.0, src/ops/dense_matmul_id_auto.rs:
+//   * fn calibration_buffers: the calibration inputs -- adversarial
+//     activations (eight bases including 1 + 2^-23, scaled by
+//     1 + ((17 i) mod 11) / 4096), the balanced and skewed routing profiles,
+//     outputs poisoned with a guard past the end;
+//   * fn calibrate_one_inner: per profile, a Direct proof, a Grouped proof,
+//     a bitwise comparison of the two, then five timing rounds that
+//     alternate which form runs first;
+//   * the winner rule: Grouped is chosen only if, on both profiles, its
+//     median wall time is at most 0.95 x Direct's, its 75th-percentile wall
+//     time is below Direct's 25th percentile, and its median GPU time is at
+//     most 1.02 x Direct's; a failed Direct proof aborts, any Grouped
+//     failure or difference in bits keeps Direct;
+//   * fn resolve_dense_matmul_id_auto_route: an exact calibrated shape
+//     takes its frozen route; a shape that differs from a calibrated one
+//     only in m takes Direct; anything else fails before any work is
+//     enqueued.
+// Every proof and timing sample is a synchronous round trip; calibration is
+// an activation-time step, not part of the hot path.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "eidm.h"
+#include "eidm_internal.hpp"
+
+struct eidm_plan {
+    std::mutex mu;
+    bool frozen = false;
+    struct Entry {
+        eidm_shape shape;
+        int route;
+    };
+    std::vector<Entry> entries;
+};
+
+namespace {
+
+using eidm::api_fail;
+using eidm::api_ok;
+
+constexpr uint32_t kPoison = 0x7fc000c7u;  // a quiet-NaN pattern no computed value takes
+constexpr uint32_t kGuard = 16;            // poisoned elements past each output
+constexpr int kTimingRounds = 5;
+
+bool same_base(const eidm_shape& a, const eidm_shape& b) {
+    return a.weight_dtype == b.weight_dtype && a.n == b.n && a.k == b.k && a.top_k == b.top_k &&
+           a.n_experts == b.n_experts && a.expert_stride_bytes == b.expert_stride_bytes &&
+           a.input_layout == b.input_layout && a.id_multiplicity == b.id_multiplicity;
+}
+
+bool same_shape(const eidm_shape& a, const eidm_shape& b) { return same_base(a, b) && a.m == b.m; }
+
+uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
+
+// Workspace sections (256-byte aligned): activations | ids of the two
+// profiles | Direct output + guard | Grouped output + guard | grouped
+// scratch | proof counters.
+struct Layout {
+    uint64_t x, ids0, ids1, yd, yg, scratch, counters, total;
+    uint64_t input_elements, routed, output_elements, scratch_bytes;
+    bool grouped_legal;
+};
+
+int layout_for(const eidm_shape* shape, Layout* l) {
+    eidm_requirements rd{}, rg{};
+    rd.struct_size = sizeof(rd);
+    rg.struct_size = sizeof(rg);
+    int rc = eidm_query(shape, EIDM_ROUTE_DIRECT, &rd);
+    if (rc) return rc;
+    l->grouped_legal = eidm_query(shape, EIDM_ROUTE_GROUPED, &rg) == EIDM_OK && rg.grouped_legal;
+    l->input_elements = rd.input_elements;
+    l->routed = rd.ids_elements;
+    l->output_elements = rd.output_elements;
+    l->scratch_bytes = l->grouped_legal ? rg.scratch_bytes : 0;
+    uint64_t off = 0;
+    l->x = off;
+    off = align256(off + l->input_elements * 4);
+    l->ids0 = off;
+    off = align256(off + l->routed * 4);
+    l->ids1 = off;
+    off = align256(off + l->routed * 4);
+    l->yd = off;
+    off = align256(off + (l->output_elements + kGuard) * 4);
+    l->yg = off;
+    off = align256(off + (l->output_elements + kGuard) * 4);
+    l->scratch = off;
+    off = align256(off + l->scratch_bytes);
+    l->counters = off;
+    l->total = off + 4 * sizeof(unsigned long long);
+    return api_ok();
+}
+
+// The calibration activations (fn calibration_buffers): element i of the
+// input takes base[(5 i + i / k) mod 8] scaled by 1 + ((17 i) mod 11) / 4096.
+std::vector<float> adversarial_activations(uint64_t elements, uint32_t k) {
+    uint32_t b2 = 0x3f800001u, b3 = 0xbf800001u;
+    float base[8] = {1.0009766f, -1.0009766f, 0.0f, 0.0f, 0.33333334f, -0.14285715f, 0.000012345679f,
+                     -0.000009765625f};
+    std::memcpy(&base[2], &b2, 4);
+    std::memcpy(&base[3], &b3, 4);
+    std::vector<float> x(elements);
+    for (uint64_t i = 0; i < elements; ++i) {
+        const float scale = 1.0f + (float)((i * 17) % 11) / 4096.0f;
+        x[i] = base[(i * 5 + i / k) % 8] * scale;
+    }
+    return x;
+}
+
+// Routing profiles (fn calibration_buffers): balanced ids (t + s) mod E, so
+// every expert gets the same number of rows; skewed ids s mod E, so all the
+// rows land on the first top_k experts.
+std::vector<uint32_t> profile_ids(uint32_t m, uint32_t top_k, uint32_t n_experts, int skewed) {
+    std::vector<uint32_t> ids((uint64_t)m * top_k);
+    for (uint32_t t = 0; t < m; ++t)
+        for (uint32_t s = 0; s < top_k; ++s)
+            ids[(uint64_t)t * top_k + s] = skewed ? s % n_experts : (uint32_t)(((uint64_t)t + s) % n_experts);
+    return ids;
+}
+
+// counters: [0] Direct elements still poisoned, [1] Grouped elements still
+// poisoned, [2] elements whose bits differ, [3] guard elements overwritten
+__global__ __launch_bounds__(256) void proof_kernel(const uint32_t* __restrict__ yd, const uint32_t* __restrict__ yg,
+                                                    uint64_t count, int with_grouped,
+                                                    unsigned long long* __restrict__ counters) {
+    unsigned long long c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count + kGuard;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint32_t d = yd[i];
+        const uint32_t g = with_grouped ? yg[i] : kPoison;
+        if (i < count) {
+            c0 += d == kPoison;
+            c1 += with_grouped && g == kPoison;
+            c2 += with_grouped && d != g;
+        } else {
+            c3 += d != kPoison || g != kPoison;
+        }
+    }
+    if (c0) atomicAdd(&counters[0], c0);
+    if (c1) atomicAdd(&counters[1], c1);
+    if (c2) atomicAdd(&counters[2], c2);
+    if (c3) atomicAdd(&counters[3], c3);
+}
+
+double pick(std::vector<double> v, int which) {  // 0: p25, 1: median, 2: p75 (the page's picks)
+    std::sort(v.begin(), v.end());
+    const size_t n = v.size();
+    if (which == 0) return v[(n - 1) / 4];
+    if (which == 1) return v[n / 2];
+    return v[3 * (n - 1) / 4];
+}
+
+int hip_fail(hipError_t err, const char* what) {
+    return api_fail(EIDM_E_DEVICE, "%s: %s", what, hipGetErrorString(err));
+}
+
+}  // namespace
+
+extern "C" {
+
+eidm_plan* eidm_plan_create(void) { return new (std::nothrow) eidm_plan(); }
+
+void eidm_plan_destroy(eidm_plan* plan) { delete plan; }
+
+int eidm_plan_freeze(eidm_plan* plan) {
+    if (!plan) return api_fail(EIDM_E_INVALID, "plan is NULL");
+    std::lock_guard<std::mutex> lock(plan->mu);
+    plan->frozen = true;
+    return api_ok();
+}
+
+int eidm_plan_route(const eidm_plan* plan, const eidm_shape* shape, int* route) {
+    if (!plan || !shape || !route) return api_fail(EIDM_E_INVALID, "plan, shape or route is NULL");
+    eidm_plan* p = const_cast<eidm_plan*>(plan);
+    std::lock_guard<std::mutex> lock(p->mu);
+    bool base = false;
+    for (const auto& e : p->entries) {
+        if (same_shape(e.shape, *shape)) {
+            *route = e.route;
+            return api_ok();
+        }
+        base = base || same_base(e.shape, *shape);
+    }
+    if (base) {  // an admitted base with an unseen m
+        *route = EIDM_ROUTE_DIRECT;
+        return api_ok();
+    }
+    return api_fail(EIDM_E_UNSUPPORTED, "shape (m=%u n=%u k=%u top_k=%u n_experts=%u) was not calibrated",
+                    shape->m, shape->n, shape->k, shape->top_k, shape->n_experts);
+}
+
+uint64_t eidm_calibration_workspace_bytes(const eidm_shape* shape) {
+    Layout l{};
+    if (!shape || layout_for(shape, &l) != EIDM_OK) return 0;
+    return l.total;
+}
+
+int eidm_calibrate(eidm_plan* plan, const eidm_shape* shape, const void* weights, uint64_t weight_bytes,
+                   void* workspace, uint64_t workspace_bytes, void* stream, eidm_calibration* receipt) {
+    if (!plan || !shape || !weights || !workspace || !receipt)
+        return api_fail(EIDM_E_INVALID, "plan, shape, weights, workspace or receipt is NULL");
+    if (receipt->struct_size != sizeof(eidm_calibration))
+        return api_fail(EIDM_E_INVALID, "receipt struct_size %u, expected %zu", receipt->struct_size,
+                        sizeof(eidm_calibration));
+    {
+        std::lock_guard<std::mutex> lock(plan->mu);
+        if (plan->frozen) return api_fail(EIDM_E_INVALID, "the plan is frozen");
+    }
+    Layout l{};
+    int rc = layout_for(shape, &l);
+    if (rc) return rc;
+    if (workspace_bytes < l.total)
+        return api_fail(EIDM_E_SIZE, "calibration needs %llu bytes of workspace, got %llu",
+                        (unsigned long long)l.total, (unsigned long long)workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256)
+        return api_fail(EIDM_E_ALIGN, "the workspace must be 256-byte aligned");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* x = reinterpret_cast<float*>(ws + l.x);
+    uint32_t* ids[2] = {reinterpret_cast<uint32_t*>(ws + l.ids0), reinterpret_cast<uint32_t*>(ws + l.ids1)};
+    float* yd = reinterpret_cast<float*>(ws + l.yd);
+    float* yg = reinterpret_cast<float*>(ws + l.yg);
+    void* scratch = l.grouped_legal ? ws + l.scratch : nullptr;
+    unsigned long long* counters = reinterpret_cast<unsigned long long*>(ws + l.counters);
+
+    eidm_calibration out{};
+    out.struct_size = sizeof(out);
+    out.grouped_legal = l.grouped_legal;
+
+    {  // inputs
+        const std::vector<float> hx = adversarial_activations(l.input_elements, shape->k);
+        hipError_t err = hipMemcpyAsync(x, hx.data(), hx.size() * 4, hipMemcpyHostToDevice, st);
+        for (int p = 0; p < 2 && err == hipSuccess; ++p) {
+            const std::vector<uint32_t> hi = profile_ids(shape->m, shape->top_k, shape->n_experts, p);
+            err = hipMemcpyAsync(ids[p], hi.data(), hi.size() * 4, hipMemcpyHostToDevice, st);
+            if (err == hipSuccess) err = hipStreamSynchronize(st);
+        }
+        if (err == hipSuccess) err = hipStreamSynchronize(st);
+        if (err != hipSuccess) return hip_fail(err, "calibration inputs");
+    }
+
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return api_fail(EIDM_E_DEVICE, "event create");
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+        (void)hipEventDestroy(ev[0]);
+        return api_fail(EIDM_E_DEVICE, "event create");
+    }
+    struct Events {
+        hipEvent_t* e;
+        ~Events() {
+            (void)hipEventDestroy(e[0]);
+            (void)hipEventDestroy(e[1]);
+        }
+    } guard_events{ev};
+
+    bool grouped_ok = l.grouped_legal;
+    bool identical = l.grouped_legal;
+    int reason = l.grouped_legal ? EIDM_CAL_GROUPED_WINS : EIDM_CAL_GROUPED_NOT_LEGAL;
+    const uint64_t out_words = l.output_elements + kGuard;
+
+    // one call of one form on profile p; wall and GPU microseconds
+    auto call = [&](int route, int p, double* wall_us, double* gpu_us) -> int {
+        float* y = route == EIDM_ROUTE_DIRECT ? yd : yg;
+        const auto t0 = std::chrono::steady_clock::now();
+        hipError_t err = hipEventRecord(ev[0], st);
+        if (err != hipSuccess) return hip_fail(err, "event record");
+        int r = eidm_matmul_id(shape, route, weights, weight_bytes, x, ids[p], y,
+                               route == EIDM_ROUTE_GROUPED ? scratch : nullptr,
+                               route == EIDM_ROUTE_GROUPED ? l.scratch_bytes : 0, stream, nullptr);
+        if (r) return r;
+        err = hipEventRecord(ev[1], st);
+        if (err == hipSuccess) err = hipStreamSynchronize(st);
+        if (err != hipSuccess) return hip_fail(err, "calibration call");
+        const auto t1 = std::chrono::steady_clock::now();
+        float ms = 0.0f;
+        err = hipEventElapsedTime(&ms, ev[0], ev[1]);
+        if (err != hipSuccess) return hip_fail(err, "event time");
+        if (wall_us) *wall_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+        if (gpu_us) *gpu_us = ms * 1e3;
+        return EIDM_OK;
+    };
+
+    for (int p = 0; p < 2; ++p) {
+        // proofs: poisoned outputs, one call of each form, then the device check
+        hipError_t err = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(yd), (int)kPoison, out_words, st);
+        if (err == hipSuccess)
+            err = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(yg), (int)kPoison, out_words, st);
+        if (err == hipSuccess) err = hipMemsetAsync(counters, 0, 4 * sizeof(unsigned long long), st);
+        if (err != hipSuccess) return hip_fail(err, "poison");
+        rc = call(EIDM_ROUTE_DIRECT, p, nullptr, nullptr);
+        if (rc) return api_fail(rc, "Direct proof failed (profile %d)", p);
+        if (grouped_ok && call(EIDM_ROUTE_GROUPED, p, nullptr, nullptr) != EIDM_OK) {
+            grouped_ok = identical = false;
+            reason = EIDM_CAL_GROUPED_FAILED;
+        }
+        const uint64_t blocks = std::min<uint64_t>((out_words + 255) / 256, 4096);
+        hipLaunchKernelGGL(proof_kernel, dim3((uint32_t)blocks), dim3(256), 0, st,
+                           reinterpret_cast<const uint32_t*>(yd), reinterpret_cast<const uint32_t*>(yg),
+                           l.output_elements, grouped_ok ? 1 : 0, counters);
+        unsigned long long c[4] = {0, 0, 0, 0};
+        err = hipGetLastError();
+        if (err == hipSuccess) err = hipMemcpyAsync(c, counters, sizeof(c), hipMemcpyDeviceToHost, st);
+        if (err == hipSuccess) err = hipStreamSynchronize(st);
+        if (err != hipSuccess) return hip_fail(err, "proof check");
+        if (c[0] != 0 || c[3] != 0)
+            return api_fail(EIDM_E_DEVICE, "Direct proof failed (profile %d): %llu outputs unwritten, %llu guard "
+                            "elements overwritten", p, c[0], c[3]);
+        if (grouped_ok && c[1] != 0) {
+            grouped_ok = identical = false;
+            reason = EIDM_CAL_GROUPED_FAILED;
+        } else if (grouped_ok && c[2] != 0) {
+            grouped_ok = identical = false;
+            reason = EIDM_CAL_NOT_IDENTICAL;
+        }
+
+        // timing: five rounds, the first form alternating
+        std::vector<double> dw, dg, gw, gg;
+        for (int round = 0; round < kTimingRounds; ++round) {
+            const int first = round % 2 == 0 ? EIDM_ROUTE_DIRECT : EIDM_ROUTE_GROUPED;
+            for (int j = 0; j < 2; ++j) {
+                const int route = j == 0 ? first : (first == EIDM_ROUTE_DIRECT ? EIDM_ROUTE_GROUPED : EIDM_ROUTE_DIRECT);
+                if (route == EIDM_ROUTE_GROUPED && !grouped_ok) continue;
+                double w = 0.0, g = 0.0;
+                rc = call(route, p, &w, &g);
+                if (rc) {
+                    if (route == EIDM_ROUTE_DIRECT) return api_fail(rc, "Direct timing failed (profile %d)", p);
+                    grouped_ok = false;
+                    reason = EIDM_CAL_GROUPED_FAILED;
+                    continue;
+                }
+                (route == EIDM_ROUTE_DIRECT ? dw : gw).push_back(w);
+                (route == EIDM_ROUTE_DIRECT ? dg : gg).push_back(g);
+            }
+        }
+        out.direct_wall_p25[p] = pick(dw, 0);
+        out.direct_wall_median[p] = pick(dw, 1);
+        out.direct_wall_p75[p] = pick(dw, 2);
+        out.direct_gpu_median[p] = pick(dg, 1);
+        if (grouped_ok && gw.size() == (size_t)kTimingRounds) {
+            out.grouped_wall_p25[p] = pick(gw, 0);
+            out.grouped_wall_median[p] = pick(gw, 1);
+            out.grouped_wall_p75[p] = pick(gw, 2);
+            out.grouped_gpu_median[p] = pick(gg, 1);
+            // the winner rule, checked profile by profile (the first failed test is the reason)
+            if (reason == EIDM_CAL_GROUPED_WINS) {
+                if (!(out.grouped_wall_median[p] <= 0.95 * out.direct_wall_median[p])) reason = EIDM_CAL_WALL_MEDIAN;
+                else if (!(out.grouped_wall_p75[p] < out.direct_wall_p25[p])) reason = EIDM_CAL_WALL_QUARTILES;
+                else if (!(out.grouped_gpu_median[p] <= 1.02 * out.direct_gpu_median[p])) reason = EIDM_CAL_GPU_MEDIAN;
+            }
+        } else if (reason == EIDM_CAL_GROUPED_WINS) {
+            reason = EIDM_CAL_GROUPED_FAILED;
+        }
+    }
+
+    out.bit_identical = identical ? 1 : 0;
+    out.reason = reason;
+    out.route = reason == EIDM_CAL_GROUPED_WINS ? EIDM_ROUTE_GROUPED : EIDM_ROUTE_DIRECT;
+    {
+        std::lock_guard<std::mutex> lock(plan->mu);
+        if (plan->frozen) return api_fail(EIDM_E_INVALID, "the plan was frozen during calibration");
+        bool replaced = false;
+        for (auto& e : plan->entries)
+            if (same_shape(e.shape, *shape)) {
+                e.route = out.route;
+                replaced = true;
+            }
+        if (!replaced) plan->entries.push_back({*shape, out.route});
+    }
+    *receipt = out;
+    return api_ok();
+}
+
+int eidm_matmul_id_planned(const eidm_plan* plan, const eidm_shape* shape, const void* weights,
+                           uint64_t weight_bytes, const float* input, const uint32_t* ids, float* output,
+                           void* scratch, uint64_t scratch_bytes, void* stream, int* route_taken) {
+    int route = 0;
+    const int rc = eidm_plan_route(plan, shape, &route);
+    if (rc) return rc;
+    return eidm_matmul_id(shape, route, weights, weight_bytes, input, ids, output, scratch, scratch_bytes,
+                          stream, route_taken);
+}
+
+}  // extern "C"

@@ -20,10 +20,12 @@
 #include "eidm_internal.hpp"
 
 namespace {
-
 thread_local std::string g_error;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+namespace eidm {
+
+int api_fail(int code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -33,10 +35,17 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
-int ok() {
+int api_ok() {
     g_error.clear();
     return EIDM_OK;
 }
+
+}  // namespace eidm
+
+namespace {
+
+using eidm::api_fail;
+int ok() { return eidm::api_ok(); }
 
 bool mul_ok(uint64_t a, uint64_t b, uint64_t* out) {
     return !__builtin_mul_overflow(a, b, out);
@@ -70,50 +79,50 @@ struct Plan {
 };
 
 int check_shape(const eidm_shape* s, Plan* p) {
-    if (!s) return fail(EIDM_E_INVALID, "shape is NULL");
+    if (!s) return api_fail(EIDM_E_INVALID, "shape is NULL");
     if (s->struct_size != sizeof(eidm_shape))
-        return fail(EIDM_E_INVALID, "shape.struct_size is %u, expected %zu", s->struct_size,
+        return api_fail(EIDM_E_INVALID, "shape.struct_size is %u, expected %zu", s->struct_size,
                     sizeof(eidm_shape));
     const int size = dtype_size(s->weight_dtype);
-    if (!size) return fail(EIDM_E_INVALID, "unknown weight dtype %d", s->weight_dtype);
+    if (!size) return api_fail(EIDM_E_INVALID, "unknown weight dtype %d", s->weight_dtype);
     if (s->input_layout != EIDM_LAYOUT_SHARED_PER_TOKEN && s->input_layout != EIDM_LAYOUT_SLOTTED)
-        return fail(EIDM_E_INVALID, "unknown input layout %d", s->input_layout);
+        return api_fail(EIDM_E_INVALID, "unknown input layout %d", s->input_layout);
     if (s->id_multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN && s->id_multiplicity != EIDM_IDS_MAY_REPEAT)
-        return fail(EIDM_E_INVALID, "unknown id multiplicity %d", s->id_multiplicity);
-    if (s->reserved0 != 0) return fail(EIDM_E_INVALID, "shape.reserved0 must be 0");
+        return api_fail(EIDM_E_INVALID, "unknown id multiplicity %d", s->id_multiplicity);
+    if (s->reserved0 != 0) return api_fail(EIDM_E_INVALID, "shape.reserved0 must be 0");
     if (!s->m || !s->n || !s->k || !s->top_k || !s->n_experts)
-        return fail(EIDM_E_INVALID, "zero dimension (m=%u n=%u k=%u top_k=%u n_experts=%u)", s->m,
+        return api_fail(EIDM_E_INVALID, "zero dimension (m=%u n=%u k=%u top_k=%u n_experts=%u)", s->m,
                     s->n, s->k, s->top_k, s->n_experts);
     if (s->n_experts > eidm::kMaxExperts)
-        return fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", s->n_experts,
+        return api_fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", s->n_experts,
                     eidm::kMaxExperts);
     if (s->id_multiplicity == EIDM_IDS_DISTINCT_PER_TOKEN && s->top_k > s->n_experts)
-        return fail(EIDM_E_INVALID, "top_k %u distinct ids from %u experts", s->top_k, s->n_experts);
+        return api_fail(EIDM_E_INVALID, "top_k %u distinct ids from %u experts", s->top_k, s->n_experts);
     if (s->n > kIndexLimit || s->k > kIndexLimit)
-        return fail(EIDM_E_UNSUPPORTED, "n or k at or above 2^31");
+        return api_fail(EIDM_E_UNSUPPORTED, "n or k at or above 2^31");
 
     uint64_t body;
     if (!mul_ok((uint64_t)s->n, s->k, &body) || !mul_ok(body, size, &body))
-        return fail(EIDM_E_INVALID, "expert size overflows");
+        return api_fail(EIDM_E_INVALID, "expert size overflows");
     if (s->expert_stride_bytes % size)
-        return fail(EIDM_E_ALIGN, "expert stride %llu is not a multiple of the dtype size %d",
+        return api_fail(EIDM_E_ALIGN, "expert stride %llu is not a multiple of the dtype size %d",
                     (unsigned long long)s->expert_stride_bytes, size);
     if (s->expert_stride_bytes < body)
-        return fail(EIDM_E_INVALID, "expert stride %llu is shorter than one expert (%llu bytes)",
+        return api_fail(EIDM_E_INVALID, "expert stride %llu is shorter than one expert (%llu bytes)",
                     (unsigned long long)s->expert_stride_bytes, (unsigned long long)body);
     uint64_t req;
     if (!mul_ok((uint64_t)(s->n_experts - 1), s->expert_stride_bytes, &req) || !add_ok(req, body, &req))
-        return fail(EIDM_E_INVALID, "required weight bytes overflow");
+        return api_fail(EIDM_E_INVALID, "required weight bytes overflow");
 
     uint64_t routed, in_rows, in_el, out_el;
-    if (!mul_ok(s->m, s->top_k, &routed)) return fail(EIDM_E_INVALID, "m*top_k overflows");
-    if (routed > kIndexLimit) return fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
+    if (!mul_ok(s->m, s->top_k, &routed)) return api_fail(EIDM_E_INVALID, "m*top_k overflows");
+    if (routed > kIndexLimit) return api_fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
     in_rows = s->input_layout == EIDM_LAYOUT_SLOTTED ? routed : s->m;
-    if (!mul_ok(in_rows, s->k, &in_el)) return fail(EIDM_E_INVALID, "input size overflows");
-    if (!mul_ok(routed, s->n, &out_el)) return fail(EIDM_E_INVALID, "output size overflows");
+    if (!mul_ok(in_rows, s->k, &in_el)) return api_fail(EIDM_E_INVALID, "input size overflows");
+    if (!mul_ok(routed, s->n, &out_el)) return api_fail(EIDM_E_INVALID, "output size overflows");
     uint64_t direct_blocks;
     if (!mul_ok((s->n + 15) / 16, routed, &direct_blocks) || direct_blocks > kIndexLimit)
-        return fail(EIDM_E_UNSUPPORTED, "Direct grid of %llu blocks is too large",
+        return api_fail(EIDM_E_UNSUPPORTED, "Direct grid of %llu blocks is too large",
                     (unsigned long long)direct_blocks);
 
     p->routed = routed;
@@ -144,7 +153,7 @@ int resolve_route(const eidm_shape* s, const Plan& p, int route, bool scratch_gi
         return EIDM_OK;
     }
     default:
-        return fail(EIDM_E_INVALID, "unknown route %d", route);
+        return api_fail(EIDM_E_INVALID, "unknown route %d", route);
     }
 }
 
@@ -165,7 +174,7 @@ int device_cus() {
 }
 
 int device_fail(hipError_t err, const char* what) {
-    return fail(EIDM_E_DEVICE, "%s: %s", what, hipGetErrorString(err));
+    return api_fail(EIDM_E_DEVICE, "%s: %s", what, hipGetErrorString(err));
 }
 
 // Validate everything a matmul call needs; fills args, map buffers and route.
@@ -177,23 +186,23 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
     int rc = check_shape(s, &p);
     if (rc) return rc;
     const int size = dtype_size(s->weight_dtype);
-    if (!weights) return fail(EIDM_E_INVALID, "weights is NULL");
-    if (!aligned(weights, size)) return fail(EIDM_E_ALIGN, "weights not aligned to %d bytes", size);
+    if (!weights) return api_fail(EIDM_E_INVALID, "weights is NULL");
+    if (!aligned(weights, size)) return api_fail(EIDM_E_ALIGN, "weights not aligned to %d bytes", size);
     if (weight_bytes < p.required_weight_bytes)
-        return fail(EIDM_E_SIZE, "weight extent %llu below the required %llu bytes",
+        return api_fail(EIDM_E_SIZE, "weight extent %llu below the required %llu bytes",
                     (unsigned long long)weight_bytes, (unsigned long long)p.required_weight_bytes);
-    if (!input || !ids || !output) return fail(EIDM_E_INVALID, "input, ids or output is NULL");
+    if (!input || !ids || !output) return api_fail(EIDM_E_INVALID, "input, ids or output is NULL");
     if (!aligned(input, 4) || !aligned(ids, 4) || !aligned(output, 4))
-        return fail(EIDM_E_ALIGN, "input, ids and output must be 4-byte aligned");
+        return api_fail(EIDM_E_ALIGN, "input, ids and output must be 4-byte aligned");
     rc = resolve_route(s, p, route, true, scratch ? scratch_bytes : 0, chosen);
     if (rc) return rc;
     if (*chosen == EIDM_ROUTE_GROUPED) {
-        if (!scratch) return fail(EIDM_E_SIZE, "Grouped route needs %llu bytes of scratch, got none",
+        if (!scratch) return api_fail(EIDM_E_SIZE, "Grouped route needs %llu bytes of scratch, got none",
                                   (unsigned long long)p.grouped_scratch);
         if (scratch_bytes < p.grouped_scratch)
-            return fail(EIDM_E_SIZE, "Grouped route needs %llu bytes of scratch, got %llu",
+            return api_fail(EIDM_E_SIZE, "Grouped route needs %llu bytes of scratch, got %llu",
                         (unsigned long long)p.grouped_scratch, (unsigned long long)scratch_bytes);
-        if (!aligned(scratch, 256)) return fail(EIDM_E_ALIGN, "scratch must be 256-byte aligned");
+        if (!aligned(scratch, 256)) return api_fail(EIDM_E_ALIGN, "scratch must be 256-byte aligned");
         uint8_t* base = static_cast<uint8_t*>(scratch);
         buf->hist = reinterpret_cast<uint32_t*>(base + p.off_hist);
         buf->counts = reinterpret_cast<uint32_t*>(base + p.off_counts);
@@ -234,31 +243,31 @@ int run_matmul(const eidm::MatmulArgs& args, const eidm::MapBuffers& buf, int ch
 
 int check_route_args(const float* logits, uint32_t m, uint32_t n_experts, uint32_t top_k,
                      const uint32_t* ids, const float* gates) {
-    if (!logits || !ids) return fail(EIDM_E_INVALID, "logits or ids is NULL");
-    if (!m || !n_experts || !top_k) return fail(EIDM_E_INVALID, "zero dimension");
+    if (!logits || !ids) return api_fail(EIDM_E_INVALID, "logits or ids is NULL");
+    if (!m || !n_experts || !top_k) return api_fail(EIDM_E_INVALID, "zero dimension");
     if (n_experts > eidm::kMaxExperts)
-        return fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", n_experts,
+        return api_fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", n_experts,
                     eidm::kMaxExperts);
-    if (top_k > n_experts) return fail(EIDM_E_INVALID, "top_k %u above n_experts %u", top_k, n_experts);
+    if (top_k > n_experts) return api_fail(EIDM_E_INVALID, "top_k %u above n_experts %u", top_k, n_experts);
     if (top_k > eidm::kMaxRouterTopK)
-        return fail(EIDM_E_UNSUPPORTED, "router top_k %u above the supported %u", top_k,
+        return api_fail(EIDM_E_UNSUPPORTED, "router top_k %u above the supported %u", top_k,
                     eidm::kMaxRouterTopK);
     uint64_t tmp;
-    if (!mul_ok(m, n_experts, &tmp) || tmp > (1ull << 40)) return fail(EIDM_E_INVALID, "m*n_experts too large");
-    if ((uint64_t)m + 3 > kIndexLimit * 4) return fail(EIDM_E_UNSUPPORTED, "m too large");
+    if (!mul_ok(m, n_experts, &tmp) || tmp > (1ull << 40)) return api_fail(EIDM_E_INVALID, "m*n_experts too large");
+    if ((uint64_t)m + 3 > kIndexLimit * 4) return api_fail(EIDM_E_UNSUPPORTED, "m too large");
     if (!aligned(logits, 4) || !aligned(ids, 4) || (gates && !aligned(gates, 4)))
-        return fail(EIDM_E_ALIGN, "logits, ids and gates must be 4-byte aligned");
+        return api_fail(EIDM_E_ALIGN, "logits, ids and gates must be 4-byte aligned");
     return EIDM_OK;
 }
 
 int check_combine_args(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const float* gates,
                        const float* out) {
-    if (!y || !gates || !out) return fail(EIDM_E_INVALID, "y, gates or out is NULL");
-    if (!m || !top_k || !n) return fail(EIDM_E_INVALID, "zero dimension");
+    if (!y || !gates || !out) return api_fail(EIDM_E_INVALID, "y, gates or out is NULL");
+    if (!m || !top_k || !n) return api_fail(EIDM_E_INVALID, "zero dimension");
     uint64_t t;
-    if (!mul_ok(m, top_k, &t) || !mul_ok(t, n, &t)) return fail(EIDM_E_INVALID, "y size overflows");
+    if (!mul_ok(m, top_k, &t) || !mul_ok(t, n, &t)) return api_fail(EIDM_E_INVALID, "y size overflows");
     if (!aligned(y, 4) || !aligned(gates, 4) || !aligned(out, 4))
-        return fail(EIDM_E_ALIGN, "y, gates and out must be 4-byte aligned");
+        return api_fail(EIDM_E_ALIGN, "y, gates and out must be 4-byte aligned");
     return EIDM_OK;
 }
 
@@ -271,9 +280,9 @@ int eidm_abi_version(void) { return EIDM_ABI_VERSION; }
 const char* eidm_last_error(void) { return g_error.c_str(); }
 
 int eidm_query(const eidm_shape* shape, int route, eidm_requirements* out) {
-    if (!out) return fail(EIDM_E_INVALID, "requirements is NULL");
+    if (!out) return api_fail(EIDM_E_INVALID, "requirements is NULL");
     if (out->struct_size != sizeof(eidm_requirements))
-        return fail(EIDM_E_INVALID, "requirements.struct_size is %u, expected %zu", out->struct_size,
+        return api_fail(EIDM_E_INVALID, "requirements.struct_size is %u, expected %zu", out->struct_size,
                     sizeof(eidm_requirements));
     Plan p;
     int rc = check_shape(shape, &p);
@@ -302,7 +311,7 @@ int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t
                     uint32_t top_k, int renormalize, uint32_t* ids, float* gates, void* stream) {
     int rc = check_route_args(logits, m, n_experts, top_k, ids, gates);
     if (rc) return rc;
-    if (bias && !aligned(bias, 4)) return fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
+    if (bias && !aligned(bias, 4)) return api_fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
     hipError_t err = eidm::launch_route(logits, bias, m, n_experts, top_k, renormalize, ids, gates,
                                         static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return device_fail(err, "route launch");
@@ -311,20 +320,20 @@ int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t
 
 int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts, uint32_t* counts,
              uint32_t* offsets, uint32_t* rows, void* scratch, uint64_t scratch_bytes, void* stream) {
-    if (!ids || !counts || !offsets || !rows) return fail(EIDM_E_INVALID, "a map buffer is NULL");
-    if (!m || !top_k || !n_experts) return fail(EIDM_E_INVALID, "zero dimension");
+    if (!ids || !counts || !offsets || !rows) return api_fail(EIDM_E_INVALID, "a map buffer is NULL");
+    if (!m || !top_k || !n_experts) return api_fail(EIDM_E_INVALID, "zero dimension");
     if (n_experts > eidm::kMaxExperts)
-        return fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", n_experts,
+        return api_fail(EIDM_E_UNSUPPORTED, "n_experts %u above the supported %u", n_experts,
                     eidm::kMaxExperts);
     uint64_t routed;
     if (!mul_ok(m, top_k, &routed) || routed > kIndexLimit)
-        return fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
+        return api_fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
     const uint64_t need = eidm::map_hist_elements(routed, n_experts) * 4;
     if (!scratch || scratch_bytes < need)
-        return fail(EIDM_E_SIZE, "map needs %llu bytes of scratch", (unsigned long long)need);
+        return api_fail(EIDM_E_SIZE, "map needs %llu bytes of scratch", (unsigned long long)need);
     if (!aligned(scratch, 4) || !aligned(ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
         !aligned(rows, 4))
-        return fail(EIDM_E_ALIGN, "map buffers must be 4-byte aligned");
+        return api_fail(EIDM_E_ALIGN, "map buffers must be 4-byte aligned");
     eidm::MapBuffers buf{static_cast<uint32_t*>(scratch), counts, offsets, rows};
     hipError_t err = eidm::launch_map(ids, (uint32_t)routed, n_experts, buf,
                                       static_cast<hipStream_t>(stream));
@@ -335,14 +344,14 @@ int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts
 int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
                       int multiplicity, int32_t* bad_index_out, void* stream) {
     static std::mutex serial;  // the kernel reports through one device word
-    if (!ids || !bad_index_out) return fail(EIDM_E_INVALID, "ids or bad_index_out is NULL");
-    if (!m || !top_k || !n_experts) return fail(EIDM_E_INVALID, "zero dimension");
+    if (!ids || !bad_index_out) return api_fail(EIDM_E_INVALID, "ids or bad_index_out is NULL");
+    if (!m || !top_k || !n_experts) return api_fail(EIDM_E_INVALID, "zero dimension");
     if (multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN && multiplicity != EIDM_IDS_MAY_REPEAT)
-        return fail(EIDM_E_INVALID, "unknown id multiplicity %d", multiplicity);
+        return api_fail(EIDM_E_INVALID, "unknown id multiplicity %d", multiplicity);
     uint64_t routed;
     if (!mul_ok(m, top_k, &routed) || routed > kIndexLimit)
-        return fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
-    if (!aligned(ids, 4)) return fail(EIDM_E_ALIGN, "ids must be 4-byte aligned");
+        return api_fail(EIDM_E_UNSUPPORTED, "m*top_k at or above 2^31");
+    if (!aligned(ids, 4)) return api_fail(EIDM_E_ALIGN, "ids must be 4-byte aligned");
     int first_bad = -1;
     {
         std::lock_guard<std::mutex> lock(serial);
@@ -353,7 +362,7 @@ int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t 
     }
     *bad_index_out = first_bad;
     if (first_bad >= 0)
-        return fail(EIDM_E_IDS, "ids[%d] (token %u, slot %u) names no expert or repeats an earlier slot",
+        return api_fail(EIDM_E_IDS, "ids[%d] (token %u, slot %u) names no expert or repeats an earlier slot",
                     first_bad, (unsigned)(first_bad / top_k), (unsigned)(first_bad % top_k));
     return ok();
 }
@@ -387,8 +396,8 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
                      uint32_t* ids, float* gates, float* y, float* out, void* scratch,
                      uint64_t scratch_bytes, void* stream, int* route_taken) {
     if (shape && shape->id_multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN)
-        return fail(EIDM_E_INVALID, "the router produces distinct ids; use DISTINCT_PER_TOKEN");
-    if (!gates) return fail(EIDM_E_INVALID, "gates is NULL");
+        return api_fail(EIDM_E_INVALID, "the router produces distinct ids; use DISTINCT_PER_TOKEN");
+    if (!gates) return api_fail(EIDM_E_INVALID, "gates is NULL");
     eidm::MatmulArgs args{};
     eidm::MapBuffers buf{};
     int chosen = 0;
@@ -397,7 +406,7 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
     if (rc) return rc;
     rc = check_route_args(logits, shape->m, shape->n_experts, shape->top_k, ids, gates);
     if (rc) return rc;
-    if (bias && !aligned(bias, 4)) return fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
+    if (bias && !aligned(bias, 4)) return api_fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
     rc = check_combine_args(shape->m, shape->top_k, shape->n, y, gates, out);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -38,6 +38,10 @@ uint32_t map_waves(uint32_t n_experts);
 uint32_t map_blocks(uint64_t routed_rows, uint32_t n_experts);
 uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts);
 
+// error state of the C ABI (thread-local message; see eidm_last_error)
+int api_fail(int code, const char* fmt, ...);
+int api_ok();
+
 hipError_t launch_route(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,
                         uint32_t top_k, int renormalize, uint32_t* ids, float* gates,
                         hipStream_t stream);

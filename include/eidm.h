@@ -255,6 +255,83 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights,
                      float* out, void* scratch, uint64_t scratch_bytes, void* stream,
                      int* route_taken);
 
+/*
+ * Activation-time route calibration and the frozen plan (mlx-native
+ * dense_matmul_id_auto.rs: fn calibration_buffers, fn calibrate_one_inner
+ * and its winner rule, fn resolve_dense_matmul_id_auto_route).
+ *
+ * eidm_calibrate runs, for one exact shape and the caller's weights, on each
+ * of two routing profiles (balanced ids (t+s) mod n_experts; skewed ids
+ * s mod n_experts) with the page's adversarial activations:
+ *   1. a Direct proof and a Grouped proof on poisoned outputs with a guard:
+ *      every output must be overwritten, the guard untouched, and Grouped's
+ *      bits equal to Direct's;
+ *   2. five timing rounds, alternating which form runs first; each call is
+ *      timed by the host clock around launch + synchronisation (wall) and by
+ *      HIP events on `stream` (GPU).
+ * Grouped is chosen only if, on both profiles, its median wall time is at
+ * most 0.95 x Direct's, its 75th-percentile wall time is below Direct's
+ * 25th percentile and its median GPU time is at most 1.02 x Direct's
+ * (percentiles of 5 sorted samples v: v[1], v[2], v[3]).  A failed Direct
+ * proof aborts (EIDM_E_DEVICE); any Grouped failure or difference keeps
+ * Direct.  The decision is stored in the plan for the exact shape.
+ * Synchronous; not capturable in a graph; the workspace belongs to the call.
+ */
+typedef struct eidm_plan eidm_plan; /* opaque; host memory owned by the library */
+
+typedef enum eidm_calibration_reason {
+    EIDM_CAL_GROUPED_WINS = 0,      /* every test passed: Grouped */
+    EIDM_CAL_GROUPED_NOT_LEGAL = 1, /* Grouped cannot run this shape */
+    EIDM_CAL_GROUPED_FAILED = 2,    /* a Grouped call failed or left outputs unwritten */
+    EIDM_CAL_NOT_IDENTICAL = 3,     /* Grouped's bits differ from Direct's */
+    EIDM_CAL_WALL_MEDIAN = 4,       /* median wall time above 0.95 x Direct's */
+    EIDM_CAL_WALL_QUARTILES = 5,    /* 75th-percentile wall not below Direct's 25th */
+    EIDM_CAL_GPU_MEDIAN = 6         /* median GPU time above 1.02 x Direct's */
+} eidm_calibration_reason;
+
+typedef struct eidm_calibration {
+    uint32_t struct_size;  /* set to sizeof(eidm_calibration) by the caller */
+    int32_t route;         /* the route stored for the shape */
+    int32_t grouped_legal; /* Grouped could run the shape */
+    int32_t bit_identical; /* Grouped reproduced Direct's bits on both profiles */
+    int32_t reason;        /* eidm_calibration_reason */
+    int32_t reserved0;
+    /* per profile (0 balanced, 1 skewed), microseconds over 5 samples;
+     * the grouped_* fields are 0 when Grouped did not run */
+    double direct_wall_p25[2], direct_wall_median[2], direct_wall_p75[2], direct_gpu_median[2];
+    double grouped_wall_p25[2], grouped_wall_median[2], grouped_wall_p75[2], grouped_gpu_median[2];
+} eidm_calibration;
+
+/* A new empty plan (NULL when out of host memory); destroy with
+ * eidm_plan_destroy.  A plan may be shared by threads. */
+eidm_plan* eidm_plan_create(void);
+void eidm_plan_destroy(eidm_plan* plan);
+
+/* Host-only: device workspace bytes eidm_calibrate needs for the shape (0 if
+ * the shape is invalid).  The workspace must be 256-byte aligned. */
+uint64_t eidm_calibration_workspace_bytes(const eidm_shape* shape);
+
+/* Calibrate one exact shape on the caller's weights (device, as in
+ * eidm_matmul_id).  workspace: device, eidm_calibration_workspace_bytes.
+ * receipt: host, struct_size set; receives the measurements and decision.
+ * Fails with EIDM_E_INVALID on a frozen plan. */
+int eidm_calibrate(eidm_plan* plan, const eidm_shape* shape, const void* weights, uint64_t weight_bytes,
+                   void* workspace, uint64_t workspace_bytes, void* stream, eidm_calibration* receipt);
+
+/* No further calibration; lookups keep working. */
+int eidm_plan_freeze(eidm_plan* plan);
+
+/* Host-only lookup: an exact calibrated shape gives its stored route; a
+ * shape equal to a calibrated one in everything but m gives Direct;
+ * anything else is EIDM_E_UNSUPPORTED. */
+int eidm_plan_route(const eidm_plan* plan, const eidm_shape* shape, int* route);
+
+/* eidm_matmul_id with the route from eidm_plan_route; fails before any work
+ * is enqueued when the plan has no route for the shape. */
+int eidm_matmul_id_planned(const eidm_plan* plan, const eidm_shape* shape, const void* weights,
+                           uint64_t weight_bytes, const float* input, const uint32_t* ids, float* output,
+                           void* scratch, uint64_t scratch_bytes, void* stream, int* route_taken);
+
 #ifdef __cplusplus
 }
 #endif

@@ -161,3 +161,36 @@ def test_validate_ids_rejects_bad_arguments_before_launch(lib):
     assert L.eidm_validate_ids(P(FAKE + 2), 4, 2, 8, 0, ctypes.byref(bad), None) == B.E_ALIGN
     assert L.eidm_validate_ids(P(FAKE), 1 << 30, 4, 8, 0, ctypes.byref(bad), None) == B.E_UNSUPPORTED
     assert bad.value == 7  # untouched on failure
+
+
+def test_calibration_struct_and_plan_rules_on_the_host(lib):
+    """Plan lifecycle and every argument check of the calibration entry points
+    run on the host before any device work."""
+    assert ctypes.sizeof(B.Calibration) == 152
+    L = lib.lib
+    P = ctypes.c_void_p
+    plan = P(L.eidm_plan_create())
+    assert plan.value
+    s = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2, B.SHARED_PER_TOKEN, B.DISTINCT_PER_TOKEN)
+    route = ctypes.c_int(-1)
+    assert L.eidm_plan_route(plan, ctypes.byref(s), ctypes.byref(route)) == B.E_UNSUPPORTED
+    assert L.eidm_matmul_id_planned(plan, ctypes.byref(s), P(FAKE), 16 * 128 * 256 * 2, P(FAKE), P(FAKE),
+                                    P(FAKE), None, 0, None, None) == B.E_UNSUPPORTED
+    need = L.eidm_calibration_workspace_bytes(ctypes.byref(s))
+    assert need > 64 * 256 * 4 + 2 * (64 * 4 * 128 + 16) * 4  # activations, two outputs with guards
+    rec = B.Calibration()
+    rec.struct_size = ctypes.sizeof(B.Calibration)
+    wb = 16 * 128 * 256 * 2
+    assert L.eidm_calibrate(None, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec)) == B.E_INVALID
+    assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need - 1, None,
+                            ctypes.byref(rec)) == B.E_SIZE
+    assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE + 64), need, None,
+                            ctypes.byref(rec)) == B.E_ALIGN
+    rec.struct_size = 8
+    assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec)) == B.E_INVALID
+    rec.struct_size = ctypes.sizeof(B.Calibration)
+    bad = B.make_shape(B.BF16, 0, 128, 256, 4, 16, 128 * 256 * 2, B.SHARED_PER_TOKEN, B.DISTINCT_PER_TOKEN)
+    assert L.eidm_calibration_workspace_bytes(ctypes.byref(bad)) == 0
+    assert L.eidm_plan_freeze(plan) == B.OK
+    assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec)) == B.E_INVALID
+    L.eidm_plan_destroy(plan)

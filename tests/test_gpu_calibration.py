@@ -1,0 +1,86 @@
+"""Activation-time route calibration and the frozen plan on the GPU
+(mlx-native dense_matmul_id_auto.rs: fn calibrate_one_inner and its winner
+rule, fn resolve_dense_matmul_id_auto_route)."""
+import numpy as np
+import pytest
+import torch
+
+from expert_id_matmul_amd import binding as B
+from expert_id_matmul_amd import workloads as W
+from helpers import to_dev, ids_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def rule(rec):
+    """The page's winner rule, recomputed from the receipt's own numbers."""
+    if not rec.grouped_legal:
+        return B.DIRECT
+    for p in range(2):
+        if not (rec.grouped_wall_median[p] <= 0.95 * rec.direct_wall_median[p]):
+            return B.DIRECT
+        if not (rec.grouped_wall_p75[p] < rec.direct_wall_p25[p]):
+            return B.DIRECT
+        if not (rec.grouped_gpu_median[p] <= 1.02 * rec.direct_gpu_median[p]):
+            return B.DIRECT
+    return B.GROUPED
+
+
+def _setup(lib, dtype, m, n, k, top_k, E, seed):
+    wl = W.Workload("cal", dtype, m, n, k, top_k, E, n * k * W.DTYPE_SIZE[dtype], W.LAYOUT_SHARED,
+                    W.IDS_DISTINCT, seed, 0.02, "random", "uniform")
+    weights = torch.empty(wl.weight_bytes, dtype=torch.uint8, device="cuda")
+    W.fill_weights(wl, weights)
+    plan = B.Plan(lib)
+    shape = B.shape_of(wl)
+    ws = torch.empty(plan.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    return wl, weights, plan, shape, ws
+
+
+@pytest.mark.parametrize("name,m,n,k,top_k,E", [
+    ("decode_like", 1, 512, 1024, 8, 64),
+    ("prefill_like", 256, 512, 1024, 8, 32),
+])
+def test_calibration_follows_the_rule_and_serves_the_plan(lib, name, m, n, k, top_k, E):
+    print(f"[case] calibrate {name}", flush=True)
+    wl, weights, plan, shape, ws = _setup(lib, W.DT_BF16, m, n, k, top_k, E, seed=80)
+    rec = plan.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
+    print("[case] receipt", {k_: v for k_, v in rec.as_dict().items() if k_ != "reserved0"}, flush=True)
+    assert rec.grouped_legal == 1
+    assert rec.bit_identical == 1, B.CAL_REASONS[rec.reason]
+    assert rec.reason not in (2, 3)
+    assert rec.route == rule(rec)
+    assert (rec.reason == 0) == (rec.route == B.GROUPED)
+    for p in range(2):
+        assert 0 < rec.direct_gpu_median[p] <= rec.direct_wall_p75[p] + 1e3
+        assert rec.direct_wall_p25[p] <= rec.direct_wall_median[p] <= rec.direct_wall_p75[p]
+        assert rec.grouped_wall_p25[p] <= rec.grouped_wall_median[p] <= rec.grouped_wall_p75[p]
+    if name == "decode_like":
+        assert rec.route == B.DIRECT  # one token: Grouped adds the map and serialises the experts
+
+    # lookups: exact shape -> stored route; same base, unseen m -> Direct; other n -> error
+    assert plan.route(shape) == rec.route
+    other_m = B.shape_of(wl.with_(m=m + 3))
+    assert plan.route(other_m) == B.DIRECT
+    with pytest.raises(B.EidmError) as e:
+        plan.route(B.shape_of(wl.with_(n=n + 8, stride=(n + 8) * k * 2)))
+    assert e.value.code == B.E_UNSUPPORTED
+
+    # the planned call runs the stored route and gives the same bits as both routes
+    x = to_dev(W.activations(wl))
+    ids = ids_to_dev(W.random_distinct_ids(wl))
+    y = torch.empty((wl.routed_rows, n), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(lib.query(shape, B.GROUPED).scratch_bytes, dtype=torch.uint8, device="cuda")
+    taken = plan.matmul_id(shape, weights, x, ids, y, scratch, weight_bytes=wl.weight_bytes)
+    assert taken == rec.route
+    for route in (B.DIRECT, B.GROUPED):
+        y2 = torch.empty_like(y)
+        lib.matmul_id(shape, route, weights, x, ids, y2, scratch, weight_bytes=wl.weight_bytes)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+    plan.freeze()
+    with pytest.raises(B.EidmError) as e:
+        plan.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
+    assert e.value.code == B.E_INVALID
+    assert plan.route(shape) == rec.route
