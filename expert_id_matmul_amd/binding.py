@@ -25,7 +25,7 @@ EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk
            "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward",
            "eidm_validate_ids", "eidm_plan_create", "eidm_plan_destroy", "eidm_plan_freeze",
            "eidm_plan_route", "eidm_calibration_workspace_bytes", "eidm_calibrate",
-           "eidm_matmul_id_planned"]
+           "eidm_matmul_id_planned", "eidm_moe_ffn_scratch_bytes", "eidm_moe_ffn"]
 
 
 class Shape(ctypes.Structure):
@@ -42,6 +42,26 @@ class Requirements(ctypes.Structure):
                 ("ids_elements", ctypes.c_uint64), ("output_elements", ctypes.c_uint64),
                 ("scratch_bytes", ctypes.c_uint64), ("grouped_legal", ctypes.c_int32),
                 ("reserved0", ctypes.c_int32)]
+
+
+class FfnShape(ctypes.Structure):
+    """eidm_ffn_shape (include/eidm.h)."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("weight_dtype", ctypes.c_int32),
+                ("m", ctypes.c_uint32), ("hidden", ctypes.c_uint32), ("inter", ctypes.c_uint32),
+                ("top_k", ctypes.c_uint32), ("n_experts", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+                ("gate_up_stride_bytes", ctypes.c_uint64), ("down_stride_bytes", ctypes.c_uint64)]
+
+
+def ffn_shape_of(fw) -> FfnShape:
+    """The eidm_ffn_shape of a workloads.FfnWorkload."""
+    size = 4 if fw.dtype == 0 else 2
+    s = FfnShape()
+    s.struct_size = ctypes.sizeof(FfnShape)
+    s.weight_dtype, s.m, s.hidden, s.inter = fw.dtype, fw.m, fw.hidden, fw.inter
+    s.top_k, s.n_experts = fw.top_k, fw.n_experts
+    s.gate_up_stride_bytes = fw.inter * fw.hidden * size
+    s.down_stride_bytes = fw.hidden * fw.inter * size
+    return s
 
 
 class Calibration(ctypes.Structure):
@@ -158,6 +178,11 @@ class Library:
         L.eidm_matmul_id_planned.restype = i32
         L.eidm_matmul_id_planned.argtypes = [P, ctypes.POINTER(Shape), P, u64, P, P, P, P, u64, P,
                                              ctypes.POINTER(ctypes.c_int)]
+        L.eidm_moe_ffn_scratch_bytes.restype = u64
+        L.eidm_moe_ffn_scratch_bytes.argtypes = [ctypes.POINTER(FfnShape)]
+        L.eidm_moe_ffn.restype = i32
+        L.eidm_moe_ffn.argtypes = [ctypes.POINTER(FfnShape), i32, P, P, u64, P, u64, P, P, P, i32, P, P, P, P,
+                                   u64, P, ctypes.POINTER(ctypes.c_int)]
         L.eidm_moe_forward.restype = i32
         L.eidm_moe_forward.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, i32, P, P, P, P,
                                        P, u64, P, ctypes.POINTER(ctypes.c_int)]
@@ -265,6 +290,30 @@ class Library:
         if rc not in (OK, E_IDS):
             self._check(rc)
         return bad.value
+
+    def moe_ffn_scratch_bytes(self, shape: FfnShape) -> int:
+        return self.lib.eidm_moe_ffn_scratch_bytes(ctypes.byref(shape))
+
+    def moe_ffn(self, shape: FfnShape, route: int, w_gate, w_up, w_down, x, logits, bias, ids, gates, out,
+                scratch, renormalize: bool = True, stream=None) -> int:
+        m, hidden, inter, top_k, E = shape.m, shape.hidden, shape.inter, shape.top_k, shape.n_experts
+        gu_bytes = min(_nbytes(w_gate), _nbytes(w_up))
+        _need("w_gate", w_gate, gu_bytes, 1)
+        _need("w_up", w_up, gu_bytes, 1)
+        _need("w_down", w_down, _nbytes(w_down), 1)
+        _need("x", x, m * hidden)
+        _need("logits", logits, m * E)
+        _need("bias", bias, E, optional=True)
+        _need("ids", ids, m * top_k)
+        _need("gates", gates, m * top_k)
+        _need("out", out, m * hidden)
+        _need("scratch", scratch, self.moe_ffn_scratch_bytes(shape), 1)
+        taken = ctypes.c_int(-1)
+        self._check(self.lib.eidm_moe_ffn(ctypes.byref(shape), route, _ptr(w_gate), _ptr(w_up), gu_bytes,
+                                          _ptr(w_down), _nbytes(w_down), _ptr(x), _ptr(logits), _ptr(bias),
+                                          int(renormalize), _ptr(ids), _ptr(gates), _ptr(out), _ptr(scratch),
+                                          _nbytes(scratch), _stream(stream), ctypes.byref(taken)))
+        return taken.value
 
 
 class Plan:

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libeidm.so")
 SOURCES = ["eidm_api.hip", "route.hip", "map.hip", "matmul_direct.hip", "matmul_grouped.hip",
-           "combine.hip", "moe_direct.hip", "validate.hip", "calibrate.hip"]
+           "combine.hip", "moe_direct.hip", "validate.hip", "calibrate.hip", "ffn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

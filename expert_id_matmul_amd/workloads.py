@@ -260,3 +260,52 @@ def modular_fill(count: int, seed: int, mul: int = 19, smul: int = 37, mod: int 
     case (17, 43, 251, 125, 257)."""
     i = np.arange(count, dtype=np.int64)
     return ((((i * mul + seed * smul) % mod).astype(np.float32) - np.float32(off)) / np.float32(div)).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# the expert FFN: gate/up (shared layout) -> silu * up -> down (slotted)
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class FfnWorkload:
+    """A seeded mixture-of-experts FFN: per expert W_gate, W_up [inter, hidden]
+    and W_down [hidden, inter] in one native dtype, N(0, w_std); tokens x
+    [m, hidden] ~ N(0, 1); routed from N(0, 1) logits with a U(-0.1, 0.1)
+    selection bias."""
+
+    name: str
+    dtype: int
+    m: int
+    hidden: int
+    inter: int
+    top_k: int
+    n_experts: int
+    seed: int
+    w_std: float
+
+    def part(self, which: str) -> Workload:
+        """The matmul_id problem of one projection ("gate", "up", "down")."""
+        size = DTYPE_SIZE[self.dtype]
+        if which in ("gate", "up"):
+            return Workload(f"{self.name}_{which}", self.dtype, self.m, self.inter, self.hidden, self.top_k,
+                            self.n_experts, self.inter * self.hidden * size, LAYOUT_SHARED, IDS_DISTINCT,
+                            self.seed * 10 + (1 if which == "gate" else 2), self.w_std, "logits", "routed")
+        return Workload(f"{self.name}_down", self.dtype, self.m, self.hidden, self.inter, self.top_k,
+                        self.n_experts, self.hidden * self.inter * size, LAYOUT_SLOTTED, IDS_DISTINCT,
+                        self.seed * 10 + 3, self.w_std, "logits", "routed")
+
+    def with_(self, **kw) -> "FfnWorkload":
+        return replace(self, **kw)
+
+
+FFN_WORKLOADS = {
+    # the prefill FFN whose projections are the prefill shapes above:
+    # gate/up [768, 2048] like the balanced config, down [2048, 768] like the down projection
+    "ffn_prefill": FfnWorkload("ffn_prefill", DT_BF16, 512, 2048, 768, 8, 128, 7, 0.02),
+}
+
+
+def ffn_inputs(fw: FfnWorkload):
+    """-> (x f32 [m, hidden], logits f32 [m, E], bias f32 [E])."""
+    gate = fw.part("gate")
+    return activations(gate), router_logits(gate), router_bias(gate)

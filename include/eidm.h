@@ -256,6 +256,44 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights,
                      int* route_taken);
 
 /*
+ * The mixture-of-experts expert FFN over routed rows (hf2q
+ * dense_ffn_arena.rs MoeFfnArena: ids/weights [seq*topk], gate_all, up_all,
+ * h_all [total_rows, m_moe] f32, y_all [total_rows, h], weighted reduce;
+ * cortiq-engine mimo_moe.rs bank_tests: sum over picks of
+ * w * down(silu(gate.x) (*) up.x)):
+ *   ids, gates = route(logits, bias)                 (eidm_route_topk)
+ *   g = matmul_id(W_gate, x), u = matmul_id(W_up, x) (shared layout, n = inter, k = hidden)
+ *   h = silu(g) * u, silu(v) = v / (1 + exp(-v))      (f32, in place over g)
+ *   y = matmul_id(W_down, h)                         (slotted layout, n = hidden, k = inter)
+ *   out = combine(y, gates)                          (eidm_combine)
+ * W_gate and W_up are [n_experts][inter][hidden] at gate_up_stride_bytes
+ * per expert (one extent, gate_up_bytes, vouched for both); W_down is
+ * [n_experts][hidden][inter] at down_stride_bytes.  x device f32
+ * [m, hidden]; logits device f32 [m, n_experts]; bias device f32
+ * [n_experts] or NULL; ids u32 / gates f32 [m, top_k] and out f32
+ * [m, hidden] receive results; scratch device, 256-byte aligned, at least
+ * eidm_moe_ffn_scratch_bytes(shape) bytes (intermediates, Grouped scratch).
+ * `route` (AUTO, DIRECT, GROUPED) applies to the three projections alike;
+ * route_taken (optional) receives the route that ran.  The router's limits
+ * apply (top_k <= min(n_experts, 64), n_experts <= 2048).
+ */
+typedef struct eidm_ffn_shape {
+    uint32_t struct_size;          /* sizeof(eidm_ffn_shape) */
+    int32_t weight_dtype;          /* eidm_dtype of all three weights */
+    uint32_t m, hidden, inter, top_k, n_experts, reserved0;
+    uint64_t gate_up_stride_bytes; /* bytes between experts of W_gate and of W_up */
+    uint64_t down_stride_bytes;    /* bytes between experts of W_down */
+} eidm_ffn_shape;
+
+/* Host-only: scratch bytes eidm_moe_ffn needs (0 if the shape is invalid). */
+uint64_t eidm_moe_ffn_scratch_bytes(const eidm_ffn_shape* shape);
+
+int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, const void* w_up,
+                 uint64_t gate_up_bytes, const void* w_down, uint64_t down_bytes, const float* x,
+                 const float* logits, const float* bias, int renormalize, uint32_t* ids, float* gates,
+                 float* out, void* scratch, uint64_t scratch_bytes, void* stream, int* route_taken);
+
+/*
  * Activation-time route calibration and the frozen plan (mlx-native
  * dense_matmul_id_auto.rs: fn calibration_buffers, fn calibrate_one_inner
  * and its winner rule, fn resolve_dense_matmul_id_auto_route).

@@ -53,6 +53,8 @@ def _load():
     lib.oracle_matmul_id_at.argtypes = [i32, u32, u32, u32, u32, u32, u64, i32, P, P, P, u64, P, P, P]
     lib.oracle_combine.restype = i32
     lib.oracle_combine.argtypes = [u32, u32, u32, P, P, P]
+    lib.oracle_moe_ffn.restype = i32
+    lib.oracle_moe_ffn.argtypes = [i32, u32, u32, u32, u32, u32, u64, u64, P, P, P, P, P, P, P, P]
     lib.oracle_map.restype = i32
     lib.oracle_map.argtypes = [P, u64, u32, P, P, P]
     _lib = lib
@@ -157,3 +159,27 @@ def id_map(ids: np.ndarray, n_experts: int):
     rows = np.empty(ids.size, dtype=np.uint32)
     _load().oracle_map(_ptr(ids), ids.size, n_experts, _ptr(counts), _ptr(offsets), _ptr(rows))
     return counts, offsets, rows
+
+
+def moe_ffn(dtype: int, m: int, hidden: int, inter: int, top_k: int, n_experts: int,
+            gu_stride: int, down_stride: int, w_gate: np.ndarray, w_up: np.ndarray,
+            w_down: np.ndarray, x: np.ndarray, ids: np.ndarray, gates: np.ndarray):
+    """-> (out f64 [m, hidden], h f64 [m*top_k, inter]) of the expert FFN."""
+    wg = _c(w_gate, np.uint8).reshape(-1)
+    wu = _c(w_up, np.uint8).reshape(-1)
+    wd = _c(w_down, np.uint8).reshape(-1)
+    assert wg.size >= required_weight_bytes(dtype, inter, hidden, n_experts, gu_stride)
+    assert wu.size >= required_weight_bytes(dtype, inter, hidden, n_experts, gu_stride)
+    assert wd.size >= required_weight_bytes(dtype, hidden, inter, n_experts, down_stride)
+    x = _c(x, np.float32)
+    ids = _c(ids, np.uint32)
+    gates = _c(gates, np.float64)
+    assert x.size == m * hidden and ids.size == m * top_k and gates.size == m * top_k
+    out = np.empty((m, hidden), dtype=np.float64)
+    h = np.empty((m * top_k, inter), dtype=np.float64)
+    rc = _load().oracle_moe_ffn(dtype, m, hidden, inter, top_k, n_experts, gu_stride, down_stride,
+                                _ptr(wg), _ptr(wu), _ptr(wd), _ptr(x), _ptr(ids), _ptr(gates),
+                                _ptr(h), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_moe_ffn failed ({rc})")
+    return out, h

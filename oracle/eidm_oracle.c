@@ -283,3 +283,67 @@ int oracle_map(const uint32_t* ids, uint64_t rows_total, uint32_t n_experts,
         }
     return 0;
 }
+
+/*
+ * The mixture-of-experts expert FFN over routed rows ([mimo] bank_tests:
+ * the exact reference output is the sum over picks of w * down(silu(gate.x)
+ * (*) up.x), in f64; [arena] MoeFfnArena: gate_all and up_all come from a
+ * shared-layout matmul_id over the token rows, h_all = silu(gate) * up, y_all
+ * from a slotted-layout matmul_id over h_all, then the weighted reduce):
+ *
+ *   g[r, j] = sum_c Wg_e[j, c] x[t, c]      (j < inter, c < hidden)
+ *   u[r, j] = sum_c Wu_e[j, c] x[t, c]
+ *   h[r, j] = silu(g[r, j]) * u[r, j],   silu(v) = v / (1 + exp(-v))
+ *   y[r, i] = sum_j Wd_e[i, j] h[r, j]      (i < hidden)
+ *   out[t, i] = sum_s gates[t, s] y[t*top_k + s, i]
+ * with e = ids[r], r = t*top_k + s; Wg, Wu are [E][inter][hidden] at
+ * gu_stride bytes per expert, Wd is [E][hidden][inter] at down_stride.
+ * Everything in double.  Pins: numpy float64 brute force on tiny shapes;
+ * silu's odd-part identity silu(v) - silu(-v) = v; W_up = 0 gives 0;
+ * doubling W_down doubles out exactly; the composition of oracle_matmul_id
+ * (gate, up) and oracle_combine with an identity down projection.
+ */
+static double silu_d(double v) { return v / (1.0 + exp(-v)); }
+
+int oracle_moe_ffn(int dtype, uint32_t m, uint32_t hidden, uint32_t inter, uint32_t top_k,
+                   uint32_t n_experts, uint64_t gu_stride, uint64_t down_stride,
+                   const void* w_gate, const void* w_up, const void* w_down, const float* x,
+                   const uint32_t* ids, const double* gates, double* h_out, double* out) {
+    int size = dtype_size(dtype);
+    if (!size || !m || !hidden || !inter || !top_k || !n_experts) return -1;
+    double* h = (double*)malloc(sizeof(double) * inter);
+    if (!h) return -2;
+    for (uint64_t t = 0; t < m; ++t)
+        for (uint32_t i = 0; i < hidden; ++i) out[t * hidden + i] = 0.0;
+    for (uint64_t t = 0; t < m; ++t)
+        for (uint32_t s = 0; s < top_k; ++s) {
+            uint64_t r = t * top_k + s;
+            uint32_t e = ids[r];
+            if (e >= n_experts) {
+                free(h);
+                return -3;
+            }
+            const float* xr = x + t * hidden;
+            const uint8_t* wg = (const uint8_t*)w_gate + (uint64_t)e * gu_stride;
+            const uint8_t* wu = (const uint8_t*)w_up + (uint64_t)e * gu_stride;
+            for (uint32_t j = 0; j < inter; ++j) {
+                double g = 0.0, u = 0.0;
+                for (uint32_t c = 0; c < hidden; ++c) {
+                    uint64_t off = ((uint64_t)j * hidden + c) * size;
+                    g += oracle_widen(dtype, wg + off) * (double)xr[c];
+                    u += oracle_widen(dtype, wu + off) * (double)xr[c];
+                }
+                h[j] = silu_d(g) * u;
+                if (h_out) h_out[r * inter + j] = h[j];
+            }
+            const uint8_t* wd = (const uint8_t*)w_down + (uint64_t)e * down_stride;
+            for (uint32_t i = 0; i < hidden; ++i) {
+                double y = 0.0;
+                for (uint32_t j = 0; j < inter; ++j)
+                    y += oracle_widen(dtype, wd + ((uint64_t)i * inter + j) * size) * h[j];
+                out[t * hidden + i] += gates[r] * y;
+            }
+        }
+    free(h);
+    return 0;
+}

@@ -194,3 +194,35 @@ def test_calibration_struct_and_plan_rules_on_the_host(lib):
     assert L.eidm_plan_freeze(plan) == B.OK
     assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec)) == B.E_INVALID
     L.eidm_plan_destroy(plan)
+
+
+def test_moe_ffn_rejects_bad_arguments_before_launch(lib):
+    L = lib.lib
+    P = ctypes.c_void_p
+    s = B.FfnShape()
+    s.struct_size = ctypes.sizeof(B.FfnShape)
+    s.weight_dtype, s.m, s.hidden, s.inter, s.top_k, s.n_experts = B.BF16, 8, 64, 32, 2, 4
+    s.gate_up_stride_bytes = 32 * 64 * 2
+    s.down_stride_bytes = 64 * 32 * 2
+    assert ctypes.sizeof(B.FfnShape) == 48
+    need = L.eidm_moe_ffn_scratch_bytes(ctypes.byref(s))
+    assert need >= (2 * 8 * 2 * 32 + 8 * 2 * 64) * 4
+    wb = 4 * 32 * 64 * 2
+    args = lambda **kw: [ctypes.byref(kw.get("shape", s)), B.AUTO, P(FAKE), P(FAKE), kw.get("gub", wb), P(FAKE),
+                         kw.get("db", wb), P(FAKE), P(FAKE), None, 1, P(FAKE), P(FAKE), P(FAKE),
+                         kw.get("scratch", P(FAKE)), kw.get("sb", need), None, None]
+    assert L.eidm_moe_ffn(*args(sb=need - 1)) == B.E_SIZE
+    assert L.eidm_moe_ffn(*args(gub=wb - 2)) == B.E_SIZE
+    assert L.eidm_moe_ffn(*args(db=wb - 2)) == B.E_SIZE
+    assert L.eidm_moe_ffn(*args(scratch=P(FAKE + 128))) == B.E_ALIGN
+    assert L.eidm_moe_ffn(*args(scratch=None)) == B.E_INVALID
+    bad = B.FfnShape.from_buffer_copy(s)
+    bad.struct_size = 40
+    assert L.eidm_moe_ffn(*args(shape=bad)) == B.E_INVALID
+    assert L.eidm_moe_ffn_scratch_bytes(ctypes.byref(bad)) == 0
+    bad = B.FfnShape.from_buffer_copy(s)
+    bad.top_k = 5  # more distinct picks than experts
+    assert L.eidm_moe_ffn(*args(shape=bad)) == B.E_INVALID
+    bad = B.FfnShape.from_buffer_copy(s)
+    bad.n_experts, bad.top_k = 4096, 65  # past the router's limits
+    assert L.eidm_moe_ffn(*args(shape=bad, gub=4096 * 32 * 64 * 2, db=4096 * 32 * 64 * 2)) == B.E_UNSUPPORTED

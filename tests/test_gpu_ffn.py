@@ -1,0 +1,79 @@
+"""The expert FFN (route -> gate/up matmul_id -> silu * up -> down matmul_id
+-> combine) on the GPU against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from expert_id_matmul_amd import binding as B
+from expert_id_matmul_amd import workloads as W
+from helpers import assert_close, to_dev, u32
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [W.FfnWorkload("ffn_bf16", W.DT_BF16, 37, 96, 72, 4, 12, 51, 0.05),
+         W.FfnWorkload("ffn_f16_ragged", W.DT_F16, 23, 130, 61, 3, 9, 52, 0.05),
+         W.FfnWorkload("ffn_f32", W.DT_F32, 16, 64, 48, 2, 6, 53, 0.1),
+         W.FfnWorkload("ffn_many_rows", W.DT_BF16, 200, 256, 256, 8, 16, 54, 0.03)]
+
+
+def _device_weights(fw):
+    out = {}
+    for w in ("gate", "up", "down"):
+        p = fw.part(w)
+        t = torch.empty(p.weight_bytes, dtype=torch.uint8, device="cuda")
+        W.fill_weights(p, t)
+        out[w] = t
+    return out
+
+
+def _run(lib, fw, wdev, x, logits, bias, route):
+    shape = B.ffn_shape_of(fw)
+    ids = torch.empty((fw.m, fw.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((fw.m, fw.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((fw.m, fw.hidden), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(lib.moe_ffn_scratch_bytes(shape), dtype=torch.uint8, device="cuda")
+    taken = lib.moe_ffn(shape, route, wdev["gate"], wdev["up"], wdev["down"], x, logits, bias, ids, gates,
+                        out, scratch)
+    torch.cuda.synchronize()
+    return taken, ids, gates, out
+
+
+@pytest.mark.parametrize("fw", SMALL, ids=lambda f: f.name)
+def test_ffn_matches_the_oracle_and_both_routes_agree_bitwise(lib, fw):
+    print(f"[case] ffn {fw.name}", flush=True)
+    wdev = _device_weights(fw)
+    xh, lh, bh = W.ffn_inputs(fw)
+    x, logits, bias = to_dev(xh), to_dev(lh), to_dev(bh)
+    t_d, ids_d, gates_d, out_d = _run(lib, fw, wdev, x, logits, bias, B.DIRECT)
+    t_g, ids_g, gates_g, out_g = _run(lib, fw, wdev, x, logits, bias, B.GROUPED)
+    assert (t_d, t_g) == (B.DIRECT, B.GROUPED)
+    assert torch.equal(out_d.view(torch.int32), out_g.view(torch.int32))
+    ids_o, gates_o, _, _ = oracle.route(lh, bh, fw.top_k)
+    assert np.array_equal(u32(ids_d), ids_o)
+    parts = {w: fw.part(w) for w in ("gate", "up", "down")}
+    raw = {w: t.cpu().numpy() for w, t in wdev.items()}
+    want, _ = oracle.moe_ffn(fw.dtype, fw.m, fw.hidden, fw.inter, fw.top_k, fw.n_experts,
+                             parts["gate"].stride, parts["down"].stride, raw["gate"], raw["up"], raw["down"],
+                             xh, ids_o, gates_o)
+    assert_close(out_d.cpu().numpy(), want, what=f"{fw.name} out")
+
+
+def test_ffn_prefill_full_size_sampled_tokens(lib):
+    """The prefill FFN (m=512, hidden 2048, inter 768, top-8 of 128 bf16
+    experts) against the oracle on sampled tokens (tokens are independent)."""
+    fw = W.FFN_WORKLOADS["ffn_prefill"]
+    print("[case] ffn prefill full size", flush=True)
+    wdev = _device_weights(fw)
+    xh, lh, bh = W.ffn_inputs(fw)
+    taken, ids, gates, out = _run(lib, fw, wdev, to_dev(xh), to_dev(lh), to_dev(bh), B.AUTO)
+    assert taken == B.GROUPED
+    ids_o, gates_o, _, _ = oracle.route(lh, bh, fw.top_k)
+    assert np.array_equal(u32(ids), ids_o)
+    tokens = np.array([0, 1, 77, 255, 300, 511])
+    parts = {w: fw.part(w) for w in ("gate", "up", "down")}
+    raw = {w: t.cpu().numpy() for w, t in wdev.items()}
+    want, _ = oracle.moe_ffn(fw.dtype, len(tokens), fw.hidden, fw.inter, fw.top_k, fw.n_experts,
+                             parts["gate"].stride, parts["down"].stride, raw["gate"], raw["up"], raw["down"],
+                             xh[tokens], ids_o[tokens], gates_o[tokens])
+    assert_close(out.cpu().numpy()[tokens], want, what="ffn prefill sampled tokens")

@@ -318,3 +318,89 @@ def test_map_is_the_stable_sort_by_expert():
     assert np.array_equal(c, np.bincount(key, minlength=13).astype(np.uint32))
     assert o[0] == 0 and np.array_equal(np.diff(o.astype(np.int64)), c.astype(np.int64))
     assert c[12] == 2
+
+
+# ---------------------------------------------------------------- expert FFN
+def _ffn_parts(fw):
+    parts = {w: fw.part(w) for w in ("gate", "up", "down")}
+    raw = {w: W.weight_bytes(p) for w, p in parts.items()}
+    return parts, raw
+
+
+def _ffn_brute(fw, raw, x, ids, gates):
+    """numpy float64 with library decoders: gather, contract, silu, contract, sum."""
+    def mats(w, rows, cols):
+        size = W.DTYPE_SIZE[fw.dtype]
+        return np.stack([to_f64_library(fw.dtype, raw[w][e * rows * cols * size:(e + 1) * rows * cols * size],
+                                        rows * cols).reshape(rows, cols) for e in range(fw.n_experts)])
+    wg, wu, wd = mats("gate", fw.inter, fw.hidden), mats("up", fw.inter, fw.hidden), mats("down", fw.hidden, fw.inter)
+    e = ids.reshape(-1).astype(np.int64)
+    xr = x.astype(np.float64)[np.arange(fw.m * fw.top_k) // fw.top_k]
+    g = np.einsum("rc,rjc->rj", xr, wg[e])
+    u = np.einsum("rc,rjc->rj", xr, wu[e])
+    h = g / (1.0 + np.exp(-g)) * u
+    y = np.einsum("rj,rij->ri", h, wd[e])
+    return (y.reshape(fw.m, fw.top_k, fw.hidden) * gates.reshape(fw.m, fw.top_k, 1)).sum(axis=1)
+
+
+FFN_SMALL = [W.FfnWorkload("ffn_tiny_f32", W.DT_F32, 5, 12, 8, 2, 4, 41, 0.3),
+             W.FfnWorkload("ffn_tiny_bf16", W.DT_BF16, 4, 16, 10, 3, 6, 42, 0.3),
+             W.FfnWorkload("ffn_tiny_f16", W.DT_F16, 3, 9, 7, 2, 5, 43, 0.3)]
+
+
+@pytest.mark.parametrize("fw", FFN_SMALL, ids=lambda f: f.name)
+def test_ffn_equals_numpy_brute_force(fw):
+    parts, raw = _ffn_parts(fw)
+    x, logits, bias = W.ffn_inputs(fw)
+    ids, gates, _, _ = oracle.route(logits, bias, fw.top_k)
+    out, h = oracle.moe_ffn(fw.dtype, fw.m, fw.hidden, fw.inter, fw.top_k, fw.n_experts,
+                            parts["gate"].stride, parts["down"].stride, raw["gate"], raw["up"], raw["down"],
+                            x, ids, gates)
+    np.testing.assert_allclose(out, _ffn_brute(fw, raw, x, ids, gates), rtol=1e-12, atol=1e-14)
+
+
+def test_ffn_silu_odd_identity_zero_up_and_linearity():
+    fw = FFN_SMALL[1]
+    parts, raw = _ffn_parts(fw)
+    x, logits, bias = W.ffn_inputs(fw)
+    ids, gates, _, _ = oracle.route(logits, bias, fw.top_k)
+    args = (fw.dtype, fw.m, fw.hidden, fw.inter, fw.top_k, fw.n_experts, parts["gate"].stride,
+            parts["down"].stride)
+    out, h = oracle.moe_ffn(*args, raw["gate"], raw["up"], raw["down"], x, ids, gates)
+    # silu(v) - silu(-v) = v: negating W_gate (exact in every dtype) gives h' with h - h' = g * u,
+    # and with W_up = W_gate that is g^2 >= 0 row by row
+    neg = raw["gate"].copy()
+    size = W.DTYPE_SIZE[fw.dtype]
+    sign_byte = np.arange(neg.size) % size == size - 1
+    neg[sign_byte] ^= 0x80
+    _, h_pos = oracle.moe_ffn(*args, raw["gate"], raw["gate"], raw["down"], x, ids, gates)
+    _, h_neg = oracle.moe_ffn(*args, neg, raw["gate"], raw["down"], x, ids, gates)
+    g_direct = oracle.matmul_id(fw.dtype, fw.m, fw.inter, fw.hidden, fw.top_k, fw.n_experts,
+                                parts["gate"].stride, W.LAYOUT_SHARED, raw["gate"], x, ids)
+    np.testing.assert_allclose(h_pos - h_neg, g_direct * g_direct, rtol=1e-12, atol=1e-15)
+    # W_up = 0 -> out = 0 exactly
+    zero, _ = oracle.moe_ffn(*args, raw["gate"], np.zeros_like(raw["up"]), raw["down"], x, ids, gates)
+    assert (zero == 0).all()
+    # doubling W_down (exact: exponent + 1 for these magnitudes) doubles out exactly
+    dbl = np.frombuffer(raw["down"].tobytes(), np.uint16).copy()
+    nz = dbl & 0x7FFF != 0
+    dbl[nz] += 0x80  # bf16 exponent field starts at bit 7
+    out2, _ = oracle.moe_ffn(*args, raw["gate"], raw["up"], dbl.view(np.uint8), x, ids, gates)
+    np.testing.assert_array_equal(out2, 2.0 * out)
+
+
+def test_ffn_with_identity_down_is_the_composition_of_pinned_steps():
+    """inter = hidden and W_down = I: out = combine(silu(gate.x) * up.x) from the
+    already pinned matmul_id and combine."""
+    fw = W.FfnWorkload("ffn_id", W.DT_F32, 4, 6, 6, 2, 3, 44, 0.5)
+    parts, raw = _ffn_parts(fw)
+    eye = np.tile(np.eye(6, dtype=np.float32).reshape(-1), fw.n_experts).view(np.uint8)
+    x, logits, bias = W.ffn_inputs(fw)
+    ids, gates, _, _ = oracle.route(logits, bias, fw.top_k)
+    out, _ = oracle.moe_ffn(fw.dtype, fw.m, 6, 6, fw.top_k, fw.n_experts, parts["gate"].stride,
+                            parts["down"].stride, raw["gate"], raw["up"], eye, x, ids, gates)
+    mm = lambda w: oracle.matmul_id(fw.dtype, fw.m, 6, 6, fw.top_k, fw.n_experts, parts["gate"].stride,
+                                    W.LAYOUT_SHARED, raw[w], x, ids)
+    g, u = mm("gate"), mm("up")
+    want = oracle.combine(g / (1.0 + np.exp(-g)) * u, gates, fw.top_k)
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=1e-15)
