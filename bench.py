@@ -251,6 +251,37 @@ def bench_prefill(lib, name: str, steps: int, warmup: int):
     return res
 
 
+# ---------------------------------------------------------------------- expert FFN
+def bench_ffn(lib, steps: int, warmup: int):
+    """The expert FFN (route, gate/up, silu * up, down, combine) on the
+    prefill FFN workload, whole calls in a graph."""
+    fw = W.FFN_WORKLOADS["ffn_prefill"]
+    shape = B.ffn_shape_of(fw)
+    wdev = {}
+    for w in ("gate", "up", "down"):
+        p = fw.part(w)
+        wdev[w] = torch.empty(p.weight_bytes, dtype=torch.uint8, device="cuda")
+        W.fill_weights(p, wdev[w])
+    xh, lh, bh = W.ffn_inputs(fw)
+    x, logits, bias = _dev(xh), _dev(lh), _dev(bh)
+    ids = torch.empty((fw.m, fw.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((fw.m, fw.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((fw.m, fw.hidden), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(lib.moe_ffn_scratch_bytes(shape), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        lib.moe_ffn(shape, B.AUTO, wdev["gate"], wdev["up"], wdev["down"], x, logits, bias, ids, gates, out,
+                    scratch)
+
+    res = Timed(step, 4).run(max(16, steps // 16), max(8, warmup // 64) if warmup else 0)
+    flops = 3 * 2.0 * fw.m * fw.top_k * fw.hidden * fw.inter
+    res["flops"] = flops
+    res["tflops"] = flops / (res["gpu_ms_per_step"] * 1e-3) / 1e12
+    del wdev
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------- counters
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_direct_kernel_decode_hbm_counters.txt")
 DECODE_SOURCES = ("moe_direct.hip", "direct_wave.hpp", "route_wave.hpp", "eidm_device.hpp",
@@ -359,6 +390,10 @@ def main():
         for name in [p for p in args.prefill.split(",") if p]:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             prefill[name] = bench_prefill(lib, name, args.steps, args.warmup)
+    ffn = None
+    if not args.no_prefill:
+        print("[bench] ffn_prefill", file=sys.stderr, flush=True)
+        ffn = bench_ffn(lib, args.steps, args.warmup)
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -394,6 +429,10 @@ def main():
                      "traffic": decode_traffic()},
         "decode_detail": dec,
         "prefill": prefill_out,
+        "ffn_prefill": None if ffn is None else {
+            "workload": "m=512 hidden=2048 inter=768 top-8 of 128 bf16 experts: route, gate/up, "
+                        "silu*up, down, combine", "ms_per_step": round(ffn["gpu_ms_per_step"], 4),
+            "tflops": round(ffn["tflops"], 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
