@@ -74,6 +74,58 @@ __device__ __forceinline__ void load_w_pieces(const uint8_t* row, int kk, u32x4 
         p[i] = *(reinterpret_cast<const u32x4*>(row + (size_t)kk * S) + i);
 }
 
+// The slice sums' recursive halving over lane bits 5, 4, 3, 2 (slices b with
+// b^8, then b^4, b^2, b^1): at each level a lane keeps half of its values and
+// adds its partner's copy of that half, so afterwards lane (b, q) holds
+// values NV/16*b .. NV/16*b + NV/16 - 1.  Lane bits 5 and 4 use the gfx950
+// half-wave and row swaps (one swap gives each lane its partner's half),
+// bits 3 and 2 DPP row rotations and shifts; the sums are those of the
+// cross-lane shuffle form (f32 addition is commutative).
+template <int NV>
+__device__ __forceinline__ void halving_exchange(float (&val)[NV], int lane) {
+    {
+        constexpr int half = NV / 2;  // lane bit 5: halves of the wave
+#pragma unroll
+        for (int jj = 0; jj < half; ++jj) {
+            const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(val[jj]), __float_as_uint(val[half + jj]),
+                                                            false, false);
+            val[jj] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    }
+    {
+        constexpr int half = NV / 4;  // lane bit 4: rows of 16
+#pragma unroll
+        for (int jj = 0; jj < half; ++jj) {
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(val[jj]), __float_as_uint(val[half + jj]),
+                                                            false, false);
+            val[jj] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+    }
+    {
+        constexpr int half = NV / 8;  // lane bit 3: rotate each row by 8
+        const bool upper = (lane & 8) != 0;
+#pragma unroll
+        for (int jj = 0; jj < half; ++jj) {
+            const float mine = upper ? val[half + jj] : val[jj];
+            const float other = upper ? val[jj] : val[half + jj];
+            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x128, 0xf, 0xf, false));
+            val[jj] = mine + got;  // row_ror:8
+        }
+    }
+    {
+        constexpr int half = NV / 16;  // lane bit 2: lanes 4 apart within each 8
+        const bool upper = (lane & 4) != 0;
+#pragma unroll
+        for (int jj = 0; jj < half; ++jj) {
+            const float mine = upper ? val[half + jj] : val[jj];
+            const float other = upper ? val[jj] : val[half + jj];
+            const float down = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x114, 0xf, 0xf, false));
+            const float up = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x104, 0xf, 0xf, false));
+            val[jj] = mine + (upper ? down : up);  // row_shr:4 / row_shl:4
+        }
+    }
+}
+
 template <int DT>
 __device__ __forceinline__ void widen_w_pieces(const u32x4 (&p)[Pieces<DT>::value], float (&w)[kGranule]) {
     if constexpr (DT == kDtypeF32) {
@@ -360,18 +412,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
             for (int c = 0; c < C; ++c)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) val[(r * C + c) * 4 + v] = acc[r][c][v];
-#pragma unroll
-        for (int level = 0; level < 4; ++level) {
-            const int mask = 32 >> level;       // lane bit exchanged
-            const int half = NV >> (level + 1); // values kept after this level
-            const bool upper = (lane & mask) != 0;
-#pragma unroll
-            for (int j = 0; j < half; ++j) {
-                const float mine = upper ? val[half + j] : val[j];
-                const float other = upper ? val[j] : val[half + j];
-                val[j] = mine + __shfl_xor(other, mask);
-            }
-        }
+        halving_exchange<NV>(val, lane);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const int o = PER * b + j;
@@ -467,14 +508,19 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         uint32_t row_begin;  // first entry of the tile in the row map
         int row_count;
     };
+    // The bucket of job jb is the last e with job_start[e] <= jb (job_start
+    // is non-decreasing; an empty bucket's start equals the next one's).
+    // Two wave-wide probes find it: every sb-th entry, then the sb entries
+    // of the chosen stretch (sb = ceil(buckets / 64) <= 64).
+    const uint32_t sb = (buckets + 63) / 64;
     auto decode = [&](uint32_t jb) {
-        uint32_t lo = 0, hi = buckets;  // job_start[lo] <= jb < job_start[hi]
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (job_start[mid] <= jb) lo = mid; else hi = mid;
-        }
+        const uint32_t ci = (uint32_t)lane * sb;
+        const uint64_t coarse = __ballot(ci < buckets && job_start[ci < buckets ? ci : 0] <= jb);
+        const uint32_t base = (63u - (uint32_t)__builtin_clzll(coarse)) * sb;  // lane 0 always holds
+        const uint32_t fi = base + (uint32_t)lane;
+        const uint64_t fine = __ballot((uint32_t)lane < sb && fi < buckets && job_start[fi < buckets ? fi : 0] <= jb);
         Job j;
-        j.e = __builtin_amdgcn_readfirstlane(lo);
+        j.e = __builtin_amdgcn_readfirstlane(base + (63u - (uint32_t)__builtin_clzll(fine)));
         const uint32_t cnt = __builtin_amdgcn_readfirstlane(cnt_s[j.e]);
         const uint32_t local = jb - __builtin_amdgcn_readfirstlane(job_start[j.e]);
         const uint32_t mtiles = (cnt + BM - 1) / BM;
@@ -587,18 +633,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
             for (int c = 0; c < C; ++c)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) val[(r * C + c) * 4 + v] = acc[r][c][v];
-#pragma unroll
-        for (int level = 0; level < 4; ++level) {
-            const int mask = 32 >> level;
-            const int half = NV >> (level + 1);
-            const bool upper = (lane & mask) != 0;
-#pragma unroll
-            for (int jj = 0; jj < half; ++jj) {
-                const float mine = upper ? val[half + jj] : val[jj];
-                const float other = upper ? val[jj] : val[half + jj];
-                val[jj] = mine + __shfl_xor(other, mask);
-            }
-        }
+        halving_exchange<NV>(val, lane);
         const bool nan_rows = j.e == a.n_experts;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
