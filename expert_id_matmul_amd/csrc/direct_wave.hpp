@@ -8,17 +8,24 @@
 //   * the round loop is a ring of D register slots: round g is consumed while
 //     rounds g+1 .. g+D-1 are in flight, and round g+D is requested as soon as
 //     slot g is free;
-//   * a slot holds this lane's weight granules and its slice's activation
-//     granule (the four lanes of one matrix-core block read the same 32
-//     bytes, which the L2 serves), so the loop has one in-order load stream
-//     and no LDS, barriers or per-lane branches;
+//   * the activation row is staged once per block in LDS when the block's
+//     threads can carry it in one pass (XS): its loads go out before the
+//     first weight rounds and are stored after them, so the copy hides under
+//     the ring's fill, and the loop's only memory requests are weights.
+//     Otherwise a slot also holds its slice's activation granule (the four
+//     lanes of one slice read the same 32 bytes, which the cache serves);
+//     either way the loop has one in-order load stream and no per-lane
+//     branches;
 //   * columns past the computed ones re-read the first one and rows are
 //     whole granules, so every vector round issues the same loads in every
 //     lane.
 // Per round (128 k), lane 4b+q (slice b, column q) holds one 8-element weight
-// granule per column group; the lanes with q == 0 feed the activation as the
-// only valid A-row of the matrix-core block.  The k tail (and rows that are
-// not 16-byte aligned) take masked loads after the ring.
+// granule per column group and accumulates its own (slice, column) element
+// with vector fmas: with a single activation row, three of the four A-rows
+// of a 4x4x1 matrix-core block would be idle, and the vector step costs half
+// the issue cycles of the matrix-core one for the same bits (the step is
+// described with the canonical order).  The k tail (and rows that are not
+// 16-byte aligned) take masked loads after the ring.
 #pragma once
 
 #include "eidm_device.hpp"
@@ -47,12 +54,57 @@ __device__ __forceinline__ void direct_widen(const u32x4_t (&p)[DirectPieces<DT>
 }
 
 // One ring slot: this lane's weight granules for its C columns and the
-// activation granule of its slice, for one round.
+// activation granule of its slice, for one round (the latter unused when the
+// activation row sits in LDS).
 template <int DT, int C>
 struct DirectSlot {
     u32x4_t w[C][DirectPieces<DT>::value];
     f32x4 x[2];
 };
+
+// Staging of one f32 activation row of k elements (k % 4 == 0, 16-byte
+// aligned) in LDS: each of the block's threads carries up to kXStageVec
+// 16-byte pieces, so a block of T threads stages rows of up to
+// 4 * kXStageVec * T elements.
+constexpr int kXStageVec = 8;
+
+__host__ __device__ constexpr bool direct_xstage_fits(uint32_t k, uint32_t threads) {
+    return (uint64_t)k <= (uint64_t)4 * kXStageVec * threads;
+}
+
+struct XStage {
+    f32x4 v[kXStageVec];
+};
+
+// Piece i of this thread: i * blockDim.x + threadIdx.x, clamped to the last
+// piece, so a pass is uniform across the block (threads past the end copy
+// the last piece again, writing the value it already has).
+__device__ __forceinline__ int xstage_piece(int i, int n4) {
+    return min(i * (int)blockDim.x + (int)threadIdx.x, n4 - 1);
+}
+
+__device__ __forceinline__ void xstage_issue(const float* xrow, int k, XStage& st) {
+    const int n4 = k >> 2;
+    const int passes = (n4 + (int)blockDim.x - 1) / (int)blockDim.x;
+#pragma unroll
+    for (int i = 0; i < kXStageVec; ++i)
+        if (i < passes) st.v[i] = reinterpret_cast<const f32x4*>(xrow)[xstage_piece(i, n4)];
+}
+
+__device__ __forceinline__ void xstage_store(float* xs, int k, const XStage& st) {
+    const int n4 = k >> 2;
+    const int passes = (n4 + (int)blockDim.x - 1) / (int)blockDim.x;
+#pragma unroll
+    for (int i = 0; i < kXStageVec; ++i)
+        if (i < passes) reinterpret_cast<f32x4*>(xs)[xstage_piece(i, n4)] = st.v[i];
+}
+
+// A wavefront of a staging block that computes no columns still takes its
+// part in the copy and the barrier (st: its issued pieces).
+__device__ __forceinline__ void xstage_only(int k, float* xs, const XStage& st) {
+    xstage_store(xs, k, st);
+    __syncthreads();
+}
 
 // Columns col0 .. col0+4C-1 of routed row r, whose expert is e (< n_experts);
 // the columns from col_end on (col0 < col_end <= n) are not computed: their
@@ -60,9 +112,15 @@ struct DirectSlot {
 // On return lane q of slice 0 (lanes 0..3) holds in v[c] the output of
 // column col0 + 4c + q (every other lane holds the same totals of its own
 // slice group); cvalid[c] says whether that column is one of the computed.
-template <int DT, int C, int D, bool NT>
+// With XS every wavefront of the block has issued the copy of the same
+// activation row (xstage_issue into xst; the row 16-byte aligned, k % 4 == 0
+// and direct_xstage_fits(k, blockDim.x)) and then calls this (or
+// xstage_only); xs is LDS for k floats.  Issuing the copy early lets its
+// latency hide under whatever the caller does before.
+template <int DT, int C, int D, bool NT, bool XS>
 __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, uint32_t e, int col0,
-                                               int col_end, float (&v)[C], bool (&cvalid)[C]) {
+                                               int col_end, float (&v)[C], bool (&cvalid)[C],
+                                               float* xs, const XStage& xst) {
     constexpr int S = DtypeSize<DT>::value;
     constexpr int NP = DirectPieces<DT>::value;
     const int lane = threadIdx.x & 63;
@@ -97,20 +155,30 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
                 else
                     s.w[c][i] = *p;
             }
-        s.x[0] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK);
-        s.x[1] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK + 4);
+        if constexpr (!XS) {
+            s.x[0] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK);
+            s.x[1] = *reinterpret_cast<const f32x4*>(xlane + g * kRoundK + 4);
+        }
     };
 
-    f32x4 acc[C];
+    float acc[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < C; ++c) acc[c] = 0.0f;
 
-    auto consume = [&](const DirectSlot<DT, C>& s) {
+    auto consume = [&](int g, const DirectSlot<DT, C>& s) {
+        f32x4 x0, x1;
+        if constexpr (XS) {
+            x0 = *reinterpret_cast<const f32x4*>(xs + g * kRoundK + b * kGranule);
+            x1 = *reinterpret_cast<const f32x4*>(xs + g * kRoundK + b * kGranule + 4);
+        } else {
+            x0 = s.x[0];
+            x1 = s.x[1];
+        }
         float x[kGranule];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = q == 0 ? s.x[0][i] : 0.0f;
-            x[4 + i] = q == 0 ? s.x[1][i] : 0.0f;
+            x[i] = x0[i];
+            x[4 + i] = x1[i];
         }
         float w[C][kGranule];
 #pragma unroll
@@ -118,7 +186,7 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
 #pragma unroll
         for (int i = 0; i < kGranule; ++i)
 #pragma unroll
-            for (int c = 0; c < C; ++c) acc[c] = mfma_step(x[i], w[c][i], acc[c]);
+            for (int c = 0; c < C; ++c) acc[c] = fma_step(x[i], w[c][i], acc[c]);
     };
 
     if (full > 0) {
@@ -130,13 +198,17 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
             fetch(min(d, full - 1), ring[d]);
             __builtin_amdgcn_sched_barrier(0);  // issue in slot order
         }
+        if constexpr (XS) {
+            xstage_store(xs, k, xst);  // waits for the activation loads only
+            __syncthreads();
+        }
         int g = 0;
         // steady state: every round refills its slot; the scheduling barrier
         // keeps rounds in order so each wait is only for the oldest slot
         for (; g + 2 * D <= full; g += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
-                consume(ring[d]);
+                consume(g + d, ring[d]);
                 fetch(g + d + D, ring[d]);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -146,15 +218,18 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
         for (int j = 0; j < 2 * D; ++j) {
             const int gg = g + j;
             if (gg < full) {
-                consume(ring[j % D]);
+                consume(gg, ring[j % D]);
                 if (gg + D < full) fetch(gg + D, ring[j % D]);
             }
         }
+    } else if constexpr (XS) {
+        xstage_store(xs, k, xst);
+        __syncthreads();
     }
     // rounds that need masked loads (k tail, or rows not 16-byte aligned)
     for (int g = full; g < rounds; ++g) {
         float x[kGranule];
-        load_input_granule(xrow, g * kRoundK + b * kGranule, k, q == 0, false, x);
+        load_input_granule(xrow, g * kRoundK + b * kGranule, k, true, false, x);
         float w[C][kGranule];
 #pragma unroll
         for (int c = 0; c < C; ++c)
@@ -163,11 +238,11 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
 #pragma unroll
         for (int i = 0; i < kGranule; ++i)
 #pragma unroll
-            for (int c = 0; c < C; ++c) acc[c] = mfma_step(x[i], w[c][i], acc[c]);
+            for (int c = 0; c < C; ++c) acc[c] = fma_step(x[i], w[c][i], acc[c]);
     }
 
 #pragma unroll
-    for (int c = 0; c < C; ++c) v[c] = slice_tree(acc[c][0]);
+    for (int c = 0; c < C; ++c) v[c] = slice_tree(acc[c]);
 }
 
 }  // namespace eidm

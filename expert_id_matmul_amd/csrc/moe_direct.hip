@@ -25,13 +25,13 @@
 #define EIDM_MOE_C 2
 #endif
 #ifndef EIDM_MOE_DEPTH
-#define EIDM_MOE_DEPTH 6
+#define EIDM_MOE_DEPTH 8
 #endif
 
 namespace eidm {
 namespace {
 
-template <int DT, int C, int D, int NV, int MAXW>
+template <int DT, int C, int D, int NV, int MAXW, bool XS>
 __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, const float* __restrict__ logits,
                                                                 const float* __restrict__ bias, int renormalize,
                                                                 uint32_t* __restrict__ ids,
@@ -39,6 +39,7 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
                                                                 float* __restrict__ out, int cols_per_block) {
     __shared__ float ys[MAXW][4 * C];
     __shared__ float gate_s[MAXW];
+    extern __shared__ __align__(16) float xs[];  // token t's activation row (XS)
     const int lane = threadIdx.x & 63;
     const int slot = threadIdx.x >> 6;
     const int b = lane >> 2, q = lane & 3;
@@ -48,6 +49,13 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     const uint32_t t = blockIdx.x / col_blocks;
     const int col0 = (int)(blockIdx.x % col_blocks) * cols_per_block;
     const int col_end = min(col0 + cols_per_block, n);
+
+    // the activation copy goes out first, under the routing
+    XStage xst;
+    if constexpr (XS) {
+        xstage_issue(a.input + (size_t)t * a.k, (int)a.k, xst);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // every wavefront scores the token and runs the selection up to its own
     // pick; the last one runs all top_k picks and forms the gates
@@ -71,7 +79,7 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
 
     float v[C];
     bool cvalid[C];
-    direct_columns<DT, C, D, true>(a, r, e, col0, col_end, v, cvalid);
+    direct_columns<DT, C, D, true, XS>(a, r, e, col0, col_end, v, cvalid, xs, xst);
     if (b == 0) {
         float* yrow = a.output + (size_t)r * a.n;
 #pragma unroll
@@ -122,8 +130,15 @@ hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bia
     const int cb = moe_cols_per_block(a.n, a.m, 4 * C, device_cus);
     const uint32_t col_blocks = (a.n + cb - 1) / cb;
     const dim3 grid(col_blocks * a.m);
-    hipLaunchKernelGGL((moe_direct_kernel<DT, C, moe_depth<DT, MAXW>(), NV, MAXW>), grid, dim3(64 * a.top_k), 0,
-                       stream, a, logits, bias, renormalize, ids, gates, out, cb);
+    constexpr int D = moe_depth<DT, MAXW>();
+    // with one activation row per token, the block's wavefronts share it
+    // through LDS when they can stage it in one pass
+    if (a.layout == 0 && a.vec && direct_xstage_fits(a.k, 64 * a.top_k))
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true>), grid, dim3(64 * a.top_k),
+                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb);
+    else
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false>), grid, dim3(64 * a.top_k), 0,
+                           stream, a, logits, bias, renormalize, ids, gates, out, cb);
     return hipGetLastError();
 }
 

@@ -60,15 +60,23 @@ template <int NV>
 __device__ __forceinline__ void route_scores(const float* __restrict__ lrow, const float* __restrict__ bias,
                                              uint32_t n_experts, RouteScores<NV>& sc) {
     const int lane = threadIdx.x & 63;
+    // all loads first (lanes past n_experts >= 1 re-read the last expert), so
+    // the wavefront waits for memory once
+    float lg[NV], bs[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const uint32_t e = min((uint32_t)v * 64 + lane, n_experts - 1);
+        lg[v] = lrow[e];
+        bs[v] = bias ? bias[e] : 0.0f;
+    }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const uint32_t e = (uint32_t)v * 64 + lane;
         sc.s[v] = 0.0f;
         sc.code[v] = 0;
         if (e < n_experts) {
-            sc.s[v] = (float)(1.0 / (1.0 + exp(-(double)lrow[e])));
-            const float sel = sc.s[v] + (bias ? bias[e] : 0.0f);
-            sc.code[v] = rank_code(sel);
+            sc.s[v] = (float)(1.0 / (1.0 + exp(-(double)lg[v])));
+            sc.code[v] = rank_code(sc.s[v] + bs[v]);
         }
     }
 }
