@@ -65,11 +65,12 @@ struct DirectSlot {
 // Staging of one f32 activation row of k elements (k % 4 == 0, 16-byte
 // aligned) in LDS: each of the block's threads carries up to kXStageVec
 // 16-byte pieces, so a block of T threads stages rows of up to
-// 4 * kXStageVec * T elements.
+// 4 * kXStageVec * T elements, and at most kXStageMaxK (32 KB of LDS).
 constexpr int kXStageVec = 8;
+constexpr uint32_t kXStageMaxK = 8192;
 
 __host__ __device__ constexpr bool direct_xstage_fits(uint32_t k, uint32_t threads) {
-    return (uint64_t)k <= (uint64_t)4 * kXStageVec * threads;
+    return k <= kXStageMaxK && (uint64_t)k <= (uint64_t)4 * kXStageVec * threads;
 }
 
 struct XStage {
@@ -99,6 +100,15 @@ __device__ __forceinline__ void xstage_store(float* xs, int k, const XStage& st)
         if (i < passes) reinterpret_cast<f32x4*>(xs)[xstage_piece(i, n4)] = st.v[i];
 }
 
+// Where direct_columns finds the activation row.
+enum : int {
+    kXFromMemory = 0,  // each slot loads its slice's granule
+    kXStageInRing = 1,  // the block stages it in LDS: direct_columns stores the
+                        // issued pieces once the weight ring is requested, then
+                        // synchronises the block
+    kXInLds = 2,        // the caller has staged it and synchronised the block
+};
+
 // A wavefront of a staging block that computes no columns still takes its
 // part in the copy and the barrier (st: its issued pieces).
 __device__ __forceinline__ void xstage_only(int k, float* xs, const XStage& st) {
@@ -112,15 +122,17 @@ __device__ __forceinline__ void xstage_only(int k, float* xs, const XStage& st) 
 // On return lane q of slice 0 (lanes 0..3) holds in v[c] the output of
 // column col0 + 4c + q (every other lane holds the same totals of its own
 // slice group); cvalid[c] says whether that column is one of the computed.
-// With XS every wavefront of the block has issued the copy of the same
-// activation row (xstage_issue into xst; the row 16-byte aligned, k % 4 == 0
-// and direct_xstage_fits(k, blockDim.x)) and then calls this (or
-// xstage_only); xs is LDS for k floats.  Issuing the copy early lets its
-// latency hide under whatever the caller does before.
-template <int DT, int C, int D, bool NT, bool XS>
+// With XM != kXFromMemory the activation row is the same for the whole
+// block, 16-byte aligned with k % 4 == 0 and direct_xstage_fits(k,
+// blockDim.x), and xs is LDS for its k floats.  With kXStageInRing every
+// wavefront of the block has issued the copy (xstage_issue into *xst) and
+// then calls this (or xstage_only): issuing the copy early lets its latency
+// hide under the ring's fill.
+template <int DT, int C, int D, bool NT, int XM>
 __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, uint32_t e, int col0,
                                                int col_end, float (&v)[C], bool (&cvalid)[C],
-                                               float* xs, const XStage& xst) {
+                                               float* xs, const XStage* xst) {
+    constexpr bool XS = XM != kXFromMemory;
     constexpr int S = DtypeSize<DT>::value;
     constexpr int NP = DirectPieces<DT>::value;
     const int lane = threadIdx.x & 63;
@@ -198,8 +210,8 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
             fetch(min(d, full - 1), ring[d]);
             __builtin_amdgcn_sched_barrier(0);  // issue in slot order
         }
-        if constexpr (XS) {
-            xstage_store(xs, k, xst);  // waits for the activation loads only
+        if constexpr (XM == kXStageInRing) {
+            xstage_store(xs, k, *xst);  // waits for the activation loads only
             __syncthreads();
         }
         int g = 0;
@@ -222,8 +234,8 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
                 if (gg + D < full) fetch(gg + D, ring[j % D]);
             }
         }
-    } else if constexpr (XS) {
-        xstage_store(xs, k, xst);
+    } else if constexpr (XM == kXStageInRing) {
+        xstage_store(xs, k, *xst);
         __syncthreads();
     }
     // rounds that need masked loads (k tail, or rows not 16-byte aligned)

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(64 * WAVES) void direct_kernel(MatmulArgs a) {
     }
     float v[C];
     bool cvalid[C];
-    direct_columns<DT, C, D, EIDM_DIRECT_NT != 0, XS>(a, r, e, col0, n, v, cvalid, xs, xst);
+    direct_columns<DT, C, D, EIDM_DIRECT_NT != 0, XS ? kXStageInRing : kXFromMemory>(a, r, e, col0, n, v, cvalid,
+                                                                                      xs, &xst);
 #pragma unroll
     for (int c = 0; c < C; ++c)
         if (b == 0 && cvalid[c]) yrow[col0 + 4 * c + q] = v[c];

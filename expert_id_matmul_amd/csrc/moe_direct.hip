@@ -3,10 +3,11 @@
 //
 // A block is one token t and one group of 4*C output columns, with one
 // wavefront per slot s < top_k:
-//   * every wavefront scores token t itself and runs the router's
-//     selection (route_wave.hpp, the router kernel's own code) up to pick s,
-//     its expert; the last wavefront runs all top_k picks and forms the
-//     gates, so picks and gates are bit for bit the router kernel's;
+//   * the block scores token t once (each expert's sigmoid by one thread,
+//     into LDS); every wavefront then runs the router's selection
+//     (route_wave.hpp, the router kernel's own code) up to pick s, its
+//     expert; the last wavefront runs all top_k picks and forms the gates,
+//     so picks and gates are bit for bit the router kernel's;
 //   * it computes its routed row t*top_k+s over the block's columns exactly
 //     as the Direct kernel does (direct_columns), and stores y;
 //   * the top_k rows of the block's columns meet in LDS and one wavefront
@@ -39,6 +40,8 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
                                                                 float* __restrict__ out, int cols_per_block) {
     __shared__ float ys[MAXW][4 * C];
     __shared__ float gate_s[MAXW];
+    __shared__ float rs_s[64 * NV];        // the token's router entries
+    __shared__ uint32_t rs_code[64 * NV];
     extern __shared__ __align__(16) float xs[];  // token t's activation row (XS)
     const int lane = threadIdx.x & 63;
     const int slot = threadIdx.x >> 6;
@@ -50,17 +53,21 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     const int col0 = (int)(blockIdx.x % col_blocks) * cols_per_block;
     const int col_end = min(col0 + cols_per_block, n);
 
-    // the activation copy goes out first, under the routing
+    // the activation copy goes out first and lands in LDS with the router
+    // entries, which the block computes once, under one barrier
     XStage xst;
     if constexpr (XS) {
         xstage_issue(a.input + (size_t)t * a.k, (int)a.k, xst);
         __builtin_amdgcn_sched_barrier(0);
     }
+    route_scores_shared<NV>(logits + (size_t)t * a.n_experts, bias, a.n_experts, rs_s, rs_code);
+    if constexpr (XS) xstage_store(xs, (int)a.k, xst);
+    __syncthreads();
 
-    // every wavefront scores the token and runs the selection up to its own
-    // pick; the last one runs all top_k picks and forms the gates
+    // every wavefront runs the selection up to its own pick; the last one
+    // runs all top_k picks and forms the gates
     RouteScores<NV> sc;
-    route_scores<NV>(logits + (size_t)t * a.n_experts, bias, a.n_experts, sc);
+    route_scores_lds<NV>(rs_s, rs_code, sc);
     uint32_t pick;
     float score;
     const float sum = route_select<NV>(sc, (uint32_t)slot + 1, pick, score);
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
 
     float v[C];
     bool cvalid[C];
-    direct_columns<DT, C, D, true, XS>(a, r, e, col0, col_end, v, cvalid, xs, xst);
+    direct_columns<DT, C, D, true, XS ? kXInLds : kXFromMemory>(a, r, e, col0, col_end, v, cvalid, xs, nullptr);
     if (b == 0) {
         float* yrow = a.output + (size_t)r * a.n;
 #pragma unroll
@@ -127,7 +134,11 @@ template <int DT, int NV, int MAXW>
 hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bias, int renormalize,
                       uint32_t* ids, float* gates, float* out, int device_cus, hipStream_t stream) {
     constexpr int C = EIDM_MOE_C;
+#ifdef EIDM_MOE_COLS
+    const int cb = EIDM_MOE_COLS;
+#else
     const int cb = moe_cols_per_block(a.n, a.m, 4 * C, device_cus);
+#endif
     const uint32_t col_blocks = (a.n + cb - 1) / cb;
     const dim3 grid(col_blocks * a.m);
     constexpr int D = moe_depth<DT, MAXW>();

@@ -56,6 +56,14 @@ struct RouteScores {
     uint32_t code[NV];   // rank code of s + bias (0 once picked, or past n_experts)
 };
 
+// One expert's entry: s = sigmoid(logit) in double rounded once to f32, and
+// the rank code of s + bias.
+__device__ __forceinline__ void route_entry(float logit, float b, float& s, uint32_t& code) {
+    s = (float)(1.0 / (1.0 + exp(-(double)logit)));
+    code = rank_code(s + b);
+}
+
+// The token's entries computed by the calling wavefront alone.
 template <int NV>
 __device__ __forceinline__ void route_scores(const float* __restrict__ lrow, const float* __restrict__ bias,
                                              uint32_t n_experts, RouteScores<NV>& sc) {
@@ -74,10 +82,49 @@ __device__ __forceinline__ void route_scores(const float* __restrict__ lrow, con
         const uint32_t e = (uint32_t)v * 64 + lane;
         sc.s[v] = 0.0f;
         sc.code[v] = 0;
-        if (e < n_experts) {
-            sc.s[v] = (float)(1.0 / (1.0 + exp(-(double)lg[v])));
-            sc.code[v] = rank_code(sc.s[v] + bs[v]);
+        if (e < n_experts) route_entry(lg[v], bs[v], sc.s[v], sc.code[v]);
+    }
+}
+
+// The token's entries computed once per block: thread i takes experts
+// i, i + blockDim.x, ... and writes them to LDS (s_lds, code_lds: 64*NV
+// entries, those past n_experts as 0).  After a barrier each wavefront reads
+// its copy with route_scores_lds.  The double-precision sigmoid is the
+// router's costliest step, so a block of W wavefronts spreads it W ways
+// instead of repeating it in every wavefront.
+template <int NV>
+__device__ __forceinline__ void route_scores_shared(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                                    uint32_t n_experts, float* s_lds, uint32_t* code_lds) {
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
+    float lg[NV], bs[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        if (i * nt < 64 * NV) {  // block-uniform
+            const uint32_t e = min((uint32_t)(i * nt + tid), n_experts - 1);
+            lg[i] = lrow[e];
+            bs[i] = bias ? bias[e] : 0.0f;
         }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = i * nt + tid;
+        if (i * nt < 64 * NV && e < 64 * NV) {
+            float s = 0.0f;
+            uint32_t code = 0;
+            if ((uint32_t)e < n_experts) route_entry(lg[i], bs[i], s, code);
+            s_lds[e] = s;
+            code_lds[e] = code;
+        }
+    }
+}
+
+template <int NV>
+__device__ __forceinline__ void route_scores_lds(const float* s_lds, const uint32_t* code_lds, RouteScores<NV>& sc) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        sc.s[v] = s_lds[v * 64 + lane];
+        sc.code[v] = code_lds[v * 64 + lane];
     }
 }
 

@@ -57,6 +57,9 @@ SMALL = [
     _wl("n1_k1", W.DT_F32, 4, 1, 1, 2, 3, seed=34),
     _wl("one_expert_top1", W.DT_F16, 17, 40, 96, 1, 1, seed=35),
     _wl("m1_decode_like", W.DT_BF16, 1, 136, 1024, 8, 64, seed=36),
+    # aligned rows too long for the Direct block to stage the activation row
+    # in LDS: Direct reads it per slice from memory
+    _wl("vec_bf16_long_k", W.DT_BF16, 3, 40, 4224, 4, 8, seed=38),
     _wl("may_repeat", W.DT_BF16, 12, 48, 256, 5, 3, mult=W.IDS_MAY_REPEAT, seed=37, ids_kind="repeat"),
     # k an even number of whole 128-element rounds: Grouped streams the rounds
     # of consecutive jobs; these give blocks several jobs each, in odd and
@@ -294,17 +297,32 @@ def test_moe_forward_small_down_projection(lib, route):
     (W.DT_F32, 2, 37, 64, 5, 300, W.LAYOUT_SLOTTED),       # > 256 experts, k below one round
     (W.DT_F16, 4, 64, 256, 16, 64, W.LAYOUT_SHARED),       # 16 slots per token
     (W.DT_BF16, 5, 48, 384, 1, 7, W.LAYOUT_SLOTTED),       # one slot
-], ids=["bf16_decode_like", "f32_many_experts", "f16_top16", "bf16_top1"])
+    (W.DT_BF16, 2, 96, 512, 8, 1000, W.LAYOUT_SHARED),     # > 256 experts, staged activation row
+    (W.DT_BF16, 1, 24, 8320, 2, 16, W.LAYOUT_SHARED),      # row too long to stage: read from memory
+], ids=["bf16_decode_like", "f32_many_experts", "f16_top16", "bf16_top1", "bf16_many_experts_shared",
+        "bf16_long_k_shared"])
 def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k, top_k, n_experts, layout):
     """With the Direct route the whole path runs as one kernel; its ids, gates,
     y and out must be the bits of route_topk -> matmul_id -> combine."""
     print(f"[case] fused moe_forward dtype={dtype} m={m} n={n} k={k} top_k={top_k} E={n_experts}", flush=True)
-    wl = _wl("fused", dtype, m, n, k, top_k, n_experts, layout=layout, seed=70 + top_k)
+    _fused_vs_three_calls(lib, _wl("fused", dtype, m, n, k, top_k, n_experts, layout=layout, seed=70 + top_k),
+                          with_bias=True, renormalize=True)
+
+
+def test_moe_forward_direct_without_bias_or_renormalisation(lib):
+    print("[case] fused moe_forward without bias, raw gates", flush=True)
+    _fused_vs_three_calls(lib, _wl("fused_plain", W.DT_BF16, 3, 40, 256, 4, 32, seed=79),
+                          with_bias=False, renormalize=False)
+
+
+def _fused_vs_three_calls(lib, wl, with_bias, renormalize):
+    m, n, top_k = wl.m, wl.n, wl.top_k
     wl = wl.with_(ids_kind="logits")
     wb = W.weight_bytes(wl)
     x = W.activations(wl)
     logits = W.router_logits(wl)
-    bias = W.router_bias(wl)
+    bias = W.router_bias(wl) if with_bias else None
+    bias_dev = to_dev(bias) if with_bias else None
     shape = B.shape_of(wl)
     wdev = to_dev(wb)
 
@@ -314,11 +332,11 @@ def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k,
                 poisoned_output(wl.routed_rows * n), poisoned_output(m * n))
 
     ids_f, gates_f, y_f, out_f = bufs()
-    taken = lib.moe_forward(shape, B.DIRECT, wdev, to_dev(x), to_dev(logits), to_dev(bias), ids_f, gates_f,
-                            y_f, out_f, None, weight_bytes=wl.weight_bytes)
+    taken = lib.moe_forward(shape, B.DIRECT, wdev, to_dev(x), to_dev(logits), bias_dev, ids_f, gates_f,
+                            y_f, out_f, None, renormalize=renormalize, weight_bytes=wl.weight_bytes)
     assert taken == B.DIRECT
     ids_s, gates_s, y_s, out_s = bufs()
-    lib.route_topk(to_dev(logits), to_dev(bias), top_k, ids_s, gates_s)
+    lib.route_topk(to_dev(logits), bias_dev, top_k, ids_s, gates_s, renormalize=renormalize)
     lib.matmul_id(shape, B.DIRECT, wdev, to_dev(x), ids_s, y_s, None, weight_bytes=wl.weight_bytes)
     lib.combine(y_s[:wl.routed_rows * n].view(wl.routed_rows, n), gates_s, out_s[:m * n].view(m, n))
     torch.cuda.synchronize()
@@ -328,7 +346,7 @@ def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k,
     assert np.array_equal(yf.view(np.uint32), check_guarded(y_s, wl.routed_rows * n).view(np.uint32))
     of = check_guarded(out_f, m * n)
     assert np.array_equal(of.view(np.uint32), check_guarded(out_s, m * n).view(np.uint32))
-    ids_o, gates_o, _, _ = oracle.route(logits, bias, top_k)
+    ids_o, gates_o, _, _ = oracle.route(logits, bias, top_k, renormalize=renormalize)
     assert np.array_equal(u32(ids_f), ids_o)
     y_o = _oracle_y(wl, wb, x, ids_o)
     assert_close(yf.reshape(wl.routed_rows, n), y_o, what="fused y")
