@@ -508,27 +508,45 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         uint32_t row_begin;  // first entry of the tile in the row map
         int row_count;
     };
-    // The bucket of job jb is the last e with job_start[e] <= jb (job_start
-    // is non-decreasing; an empty bucket's start equals the next one's).
-    // Two wave-wide probes find it: every sb-th entry, then the sb entries
-    // of the chosen stretch (sb = ceil(buckets / 64) <= 64).
-    const uint32_t sb = (buckets + 63) / 64;
-    auto decode = [&](uint32_t jb) {
-        const uint32_t ci = (uint32_t)lane * sb;
-        const uint64_t coarse = __ballot(ci < buckets && job_start[ci < buckets ? ci : 0] <= jb);
-        const uint32_t base = (63u - (uint32_t)__builtin_clzll(coarse)) * sb;  // lane 0 always holds
-        const uint32_t fi = base + (uint32_t)lane;
-        const uint64_t fine = __ballot((uint32_t)lane < sb && fi < buckets && job_start[fi < buckets ? fi : 0] <= jb);
+    // Job descriptors.  The block's jobs are job + i*gridDim.x, i = 0, 1, ...
+    // A wavefront decodes 64 of them at once, one per lane, and keeps them in
+    // three registers; a job is then three lane reads, so the per-job path
+    // has no dependent chain of LDS lookups.  Lane L of a chunk starting at
+    // index i0 holds job i0 + L: the bucket of job jb is the last e with
+    // job_start[e] <= jb (job_start is non-decreasing; an empty bucket's start
+    // equals the next one's), found by a fixed-length binary search.
+    uint32_t top = 1;
+    while (top * 2 <= buckets) top *= 2;  // largest power of two <= buckets
+    uint32_t chunk_base = 0x80000000u;    // index of the job in lane 0 (none yet)
+    uint32_t d_erc = 0, d_col0 = 0, d_rb = 0;  // bucket | row_count << 16, first column, first map entry
+    auto refill = [&](uint32_t i0) {
+        chunk_base = i0;
+        const uint64_t jb64 = (uint64_t)job + ((uint64_t)i0 + (uint64_t)lane) * gridDim.x;
+        if (jb64 < total_jobs) {
+            const uint32_t jb = (uint32_t)jb64;
+            uint32_t e = 0;
+            for (uint32_t st = top; st; st >>= 1)
+                if (e + st < buckets && job_start[e + st] <= jb) e += st;
+            const uint32_t cnt = cnt_s[e];
+            const uint32_t local = jb - job_start[e];
+            const uint32_t mtiles = (cnt + BM - 1) / BM;
+            const uint32_t nt = local / mtiles, mt = local - nt * mtiles;
+            d_erc = e | (min((uint32_t)BM, cnt - mt * BM) << 16);
+            d_col0 = nt * BN;
+            d_rb = off_s[e] + mt * BM;
+        }
+    };
+    // the block's job number i (job + i*gridDim.x < total_jobs)
+    auto decode = [&](uint32_t i) {
+        if (i - chunk_base >= 64u) refill(i);  // block-uniform
+        const int L = (int)(i - chunk_base);
+        const uint32_t erc = (uint32_t)__builtin_amdgcn_readlane((int)d_erc, L);
         Job j;
-        j.e = __builtin_amdgcn_readfirstlane(base + (63u - (uint32_t)__builtin_clzll(fine)));
-        const uint32_t cnt = __builtin_amdgcn_readfirstlane(cnt_s[j.e]);
-        const uint32_t local = jb - __builtin_amdgcn_readfirstlane(job_start[j.e]);
-        const uint32_t mtiles = (cnt + BM - 1) / BM;
-        const uint32_t nt = local / mtiles, mt = local % mtiles;
+        j.e = erc & 0xffffu;
+        j.row_count = (int)(erc >> 16);
         j.wexp = j.e < a.n_experts ? j.e : 0;
-        j.col0 = nt * BN;
-        j.row_begin = __builtin_amdgcn_readfirstlane(off_s[j.e]) + mt * BM;
-        j.row_count = (int)min((uint32_t)BM, cnt - mt * BM);
+        j.col0 = (uint32_t)__builtin_amdgcn_readlane((int)d_col0, L);
+        j.row_begin = (uint32_t)__builtin_amdgcn_readlane((int)d_rb, L);
         return j;
     };
 
@@ -657,10 +675,10 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     const uint32_t my_jobs = (total_jobs - job + gridDim.x - 1) / gridDim.x;
     Job jobs[2];
     Rows rws[2];
-    uint32_t next = job + gridDim.x;
-    jobs[0] = decode(job);
+    uint32_t next = job + gridDim.x, next_i = 1;
+    jobs[0] = decode(0);
     rws[0] = fetch_rows(jobs[0]);
-    jobs[1] = next < total_jobs ? decode(next) : jobs[0];
+    jobs[1] = next < total_jobs ? decode(next_i) : jobs[0];
     rws[1] = fetch_rows(jobs[1]);
 
     // A step is two rounds: the weights of its rounds sit in register slots
@@ -717,7 +735,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         else steps(IntC<R / 4>{});
         finish(jobs[c], rws[c]);
         next += gridDim.x;
-        jobs[c] = next < total_jobs ? decode(next) : jobs[o];
+        ++next_i;
+        jobs[c] = next < total_jobs ? decode(next_i) : jobs[o];
         rws[c] = fetch_rows(jobs[c]);
     };
     uint32_t i = 0;
