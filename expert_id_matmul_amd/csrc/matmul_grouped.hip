@@ -432,7 +432,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
 // job table (bucket counts, offsets, first job) sits in LDS, so a block never
 // waits on a dependent chain of global reads between jobs.  Arithmetic and
 // order are those of grouped_kernel.
-template <int DT, int R, int C, int WAVES>
+template <int DT, int R, int C, int WAVES, bool W32>
 __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
                                                                        const uint32_t* __restrict__ counts,
                                                                        const uint32_t* __restrict__ offsets,
@@ -453,6 +453,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     uint32_t* job_start = reinterpret_cast<uint32_t*>(smem + 4 * BM * kRoundK * sizeof(float));
     uint32_t* cnt_s = job_start + buckets + 1;            // [buckets]
     uint32_t* off_s = cnt_s + buckets;                    // [buckets]
+    uint32_t* rows_s = off_s + buckets;                   // [64 jobs][BM] row-map entries
     __shared__ uint32_t wave_tot[WAVES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         uint32_t e;          // bucket (n_experts = ids naming no expert)
         uint32_t wexp;       // expert whose weights are read (e, or 0 for that bucket)
         uint32_t col0;       // first output column of the tile
-        uint32_t row_begin;  // first entry of the tile in the row map
+        uint32_t slot;       // its place in the decoded chunk (row-map entries in LDS)
         int row_count;
     };
     // Job descriptors.  The block's jobs are job + i*gridDim.x, i = 0, 1, ...
@@ -519,8 +520,16 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     while (top * 2 <= buckets) top *= 2;  // largest power of two <= buckets
     uint32_t chunk_base = 0x80000000u;    // index of the job in lane 0 (none yet)
     uint32_t d_erc = 0, d_col0 = 0, d_rb = 0;  // bucket | row_count << 16, first column, first map entry
+    // The chunk's row-map entries are copied into LDS in the same pass (the
+    // block's threads share the 64 x BM loads), so a job's row indices are
+    // LDS reads: no global read sits in the in-order load queue between two
+    // jobs, where every later wait would wait for it too.
+    constexpr int ENT = 64 * BM, EPT = (ENT + THREADS - 1) / THREADS;
     auto refill = [&](uint32_t i0) {
         chunk_base = i0;
+        d_erc = 0;
+        d_col0 = 0;
+        d_rb = 0;
         const uint64_t jb64 = (uint64_t)job + ((uint64_t)i0 + (uint64_t)lane) * gridDim.x;
         if (jb64 < total_jobs) {
             const uint32_t jb = (uint32_t)jb64;
@@ -535,6 +544,25 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
             d_col0 = nt * BN;
             d_rb = off_s[e] + mt * BM;
         }
+        // entry (L, lr): map entry lr of chunk job L (rows past its row count
+        // read its first row); every wavefront decoded the same chunk
+        uint32_t v[EPT];
+#pragma unroll
+        for (int jj = 0; jj < EPT; ++jj) {
+            const int ent = tid + jj * THREADS;
+            if (ent < ENT) {
+                const int L = ent / BM, lr = ent % BM;
+                const uint32_t rb = (uint32_t)__shfl((int)d_rb, L);
+                const uint32_t rc = (uint32_t)__shfl((int)d_erc, L) >> 16;
+                v[jj] = rows[rb + ((uint32_t)lr < rc ? (uint32_t)lr : 0u)];
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < EPT; ++jj) {
+            const int ent = tid + jj * THREADS;
+            if (ent < ENT) rows_s[ent] = v[jj];
+        }
+        __syncthreads();
     };
     // the block's job number i (job + i*gridDim.x < total_jobs)
     auto decode = [&](uint32_t i) {
@@ -546,7 +574,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         j.row_count = (int)(erc >> 16);
         j.wexp = j.e < a.n_experts ? j.e : 0;
         j.col0 = (uint32_t)__builtin_amdgcn_readlane((int)d_col0, L);
-        j.row_begin = (uint32_t)__builtin_amdgcn_readlane((int)d_rb, L);
+        j.slot = (uint32_t)L;
         return j;
     };
 
@@ -558,17 +586,14 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         uint32_t out[PER];
     };
     auto fetch_rows = [&](const Job& j) {
+        const uint32_t* rj = rows_s + j.slot * BM;  // the job's entries, past row_count already the first
         Rows g;
 #pragma unroll
-        for (int jj = 0; jj < XPER; ++jj) {
-            const int lr = (tid + jj * THREADS) >> 5;
-            g.x[jj] = rows[j.row_begin + (lr < j.row_count ? lr : 0)];
-        }
+        for (int jj = 0; jj < XPER; ++jj) g.x[jj] = rj[(tid + jj * THREADS) >> 5];
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int o = PER * b + p;
-            const int lr = 4 * (o / (4 * C)) + o % 4;
-            g.out[p] = rows[j.row_begin + (lr < j.row_count ? lr : 0)];
+            g.out[p] = rj[4 * (o / (4 * C)) + o % 4];
         }
         return g;
     };
@@ -600,12 +625,24 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
             }
     };
     // this lane's weight granules of round g (columns past n read column n-1)
+    // With W32 (an expert's matrix spans under 4 GB) a load's address is a
+    // block-uniform base (expert and round, in scalar registers) plus a
+    // 32-bit lane offset fixed for the job, so the steady loop spends no
+    // vector instructions on 64-bit addresses.
     auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
         const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)j.wexp * a.stride;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int col = min((int)j.col0 + wave * 4 * C + 4 * c + q, n - 1);
-            load_w_pieces<DT>(base + (size_t)col * a.k * S, g * kRoundK + b * kGranule, wr.p[c]);
+            if constexpr (W32) {
+                const uint8_t* rb = base + (size_t)g * kRoundK * S;
+                const uint32_t off = (uint32_t)col * (uint32_t)a.k * (uint32_t)S + (uint32_t)(b * kGranule * S);
+#pragma unroll
+                for (int i = 0; i < Pieces<DT>::value; ++i)
+                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(rb + off + 16u * (uint32_t)i);
+            } else {
+                load_w_pieces<DT>(base + (size_t)col * a.k * S, g * kRoundK + b * kGranule, wr.p[c]);
+            }
         }
     };
 
@@ -757,8 +794,11 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
     // the streamed form needs an even number of whole vector rounds
     const bool stream_form = a.vec && a.k % (2 * kRoundK) == 0;
-    auto kernel = stream_form ? grouped_stream_kernel<DT, R, C, WAVES> : grouped_kernel<DT, R, C, WAVES>;
-    const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4) : (a.n_experts + 2);
+    const bool w32 = (uint64_t)a.n * a.k * DtypeSize<DT>::value + 256 <= 0xffffffffull;
+    auto kernel = !stream_form ? grouped_kernel<DT, R, C, WAVES>
+                  : w32        ? grouped_stream_kernel<DT, R, C, WAVES, true>
+                               : grouped_stream_kernel<DT, R, C, WAVES, false>;
+    const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4 + 64 * BM) : (a.n_experts + 2);
     const size_t lds = (stream_form ? 4 : 2) * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * WAVES, lds) != hipSuccess ||
