@@ -134,11 +134,7 @@ template <int DT, int NV, int MAXW>
 hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bias, int renormalize,
                       uint32_t* ids, float* gates, float* out, int device_cus, hipStream_t stream) {
     constexpr int C = EIDM_MOE_C;
-#ifdef EIDM_MOE_COLS
-    const int cb = EIDM_MOE_COLS;
-#else
     const int cb = moe_cols_per_block(a.n, a.m, 4 * C, device_cus);
-#endif
     const uint32_t col_blocks = (a.n + cb - 1) / cb;
     const dim3 grid(col_blocks * a.m);
     constexpr int D = moe_depth<DT, MAXW>();
