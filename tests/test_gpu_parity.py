@@ -128,6 +128,63 @@ def test_bit_identity_on_the_pages_calibration_inputs(lib, profile):
     assert np.array_equal(yd.view(np.uint32), canonical_matmul_id(wl, wb, x, ids).view(np.uint32))
 
 
+# Special operand values: each route takes its multiply-adds on a different
+# unit (Grouped on the matrix core, Direct as vector fmas), so the classes
+# where two implementations of an fma could differ are planted on purpose.
+_FINITE_F32 = np.array([0x00000001, 0x807fffff, 0x00400000, 0x80000000, 0x00000000, 0x7f7fffff, 0x00800000,
+                        0x3f800001], dtype=np.uint32)
+_NONFINITE_F32 = np.array([0x7f800000, 0xff800000, 0x7fc00001, 0xffc12345], dtype=np.uint32)
+_FINITE_16 = {
+    W.DT_F16: np.array([0x0001, 0x83ff, 0x0200, 0x8000, 0x0000, 0x7bff, 0x0400], dtype=np.uint16),
+    W.DT_BF16: np.array([0x0001, 0x807f, 0x0040, 0x8000, 0x0000, 0x7f7f, 0x0080], dtype=np.uint16),
+}
+_NONFINITE_16 = {
+    W.DT_F16: np.array([0x7c00, 0xfc00, 0x7e01, 0xfe35], dtype=np.uint16),
+    W.DT_BF16: np.array([0x7f80, 0xff80, 0x7fc1, 0xffc5], dtype=np.uint16),
+}
+
+
+def _plant(rng, bits: np.ndarray, special: np.ndarray, frac: float) -> np.ndarray:
+    bits = bits.copy()
+    where = rng.random(bits.shape) < frac
+    bits[where] = special[rng.integers(0, len(special), int(where.sum()))]
+    return bits
+
+
+@pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_F16, W.DT_BF16], ids=["f32", "f16", "bf16"])
+@pytest.mark.parametrize("k", [512, 300], ids=["streamed", "masked"])
+def test_bit_identity_with_special_values(lib, dtype, k):
+    """Subnormal, signed-zero, infinite, NaN and extreme weights and activations:
+    Direct and Grouped give the same bits (NaN for NaN), and so does the CPU
+    evaluation of the documented order."""
+    print(f"[case] special values dtype={dtype} k={k}", flush=True)
+    wl = _wl("special", dtype, 7, 40, k, 3, 5, seed=90 + dtype)
+    rng = np.random.default_rng(900 + 10 * dtype + (k % 7))
+    wb = W.weight_bytes(wl)
+    # finite specials often, infinities and NaNs rarely (most outputs stay finite)
+    if dtype == W.DT_F32:
+        wbits = _plant(rng, wb.view(np.uint32), _FINITE_F32, 0.05)
+        wb = _plant(rng, wbits, _NONFINITE_F32, 0.0005).view(np.uint8)
+    else:
+        wbits = _plant(rng, wb.view(np.uint16), _FINITE_16[dtype], 0.05)
+        wb = _plant(rng, wbits, _NONFINITE_16[dtype], 0.0005).view(np.uint8)
+    xbits = _plant(rng, W.activations(wl).view(np.uint32), _FINITE_F32, 0.05)
+    x = _plant(rng, xbits, _NONFINITE_F32, 0.0005).view(np.float32)
+    ids = _ids(wl)
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT, allow_nan=True)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED, allow_nan=True)
+    canon = canonical_matmul_id(wl, wb, x, ids)
+
+    def same(a, b):
+        both_nan = np.isnan(a) & np.isnan(b)
+        return bool(np.all(both_nan | (a.view(np.uint32) == b.view(np.uint32))))
+
+    assert np.isnan(yd).any() and np.isfinite(yd).any(), "the planted values should reach the outputs"
+    assert same(yd, yg), "Direct and Grouped differ"
+    assert same(yd, canon), "not the documented order"
+
+
 def test_modular_fill_weights(lib):
     """The page's deterministic f32 weight fill ((19 i + 37 seed) mod 257 - 128) / 263."""
     wl = _wl("modfill", W.DT_F32, 13, 31, 47, 3, 5, seed=101)
