@@ -81,6 +81,13 @@ __device__ __forceinline__ void load_w_pieces(const uint8_t* row, int kk, u32x4 
 // half-wave and row swaps (one swap gives each lane its partner's half),
 // bits 3 and 2 DPP row rotations and shifts; the sums are those of the
 // cross-lane shuffle form (f32 addition is commutative).
+// f32 value of lane (DPP control CTRL) of this row; lanes whose source lies
+// outside the row read 0 (their results are never kept).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 template <int NV>
 __device__ __forceinline__ void halving_exchange(float (&val)[NV], int lane) {
     {
@@ -102,26 +109,29 @@ __device__ __forceinline__ void halving_exchange(float (&val)[NV], int lane) {
         }
     }
     {
-        constexpr int half = NV / 8;  // lane bit 3: rotate each row by 8
+        // lane bit 3: the partner is 8 lanes away in the same row, which a
+        // row rotation by 8 reaches from every lane; each half of the row
+        // adds the partner's copy of the value it keeps (the other half's
+        // sum is discarded)
+        constexpr int half = NV / 8;
         const bool upper = (lane & 8) != 0;
 #pragma unroll
         for (int jj = 0; jj < half; ++jj) {
-            const float mine = upper ? val[half + jj] : val[jj];
-            const float other = upper ? val[jj] : val[half + jj];
-            const float got = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x128, 0xf, 0xf, false));
-            val[jj] = mine + got;  // row_ror:8
+            const float lo = val[jj] + dpp_f32<0x128>(val[jj]);                   // row_ror:8
+            const float hi = val[half + jj] + dpp_f32<0x128>(val[half + jj]);
+            val[jj] = upper ? hi : lo;
         }
     }
     {
-        constexpr int half = NV / 16;  // lane bit 2: lanes 4 apart within each 8
+        // lane bit 2: lanes 4 apart within each 8, reached by a row shift
+        // left (lower lanes) or right (upper lanes) by 4
+        constexpr int half = NV / 16;
         const bool upper = (lane & 4) != 0;
 #pragma unroll
         for (int jj = 0; jj < half; ++jj) {
-            const float mine = upper ? val[half + jj] : val[jj];
-            const float other = upper ? val[jj] : val[half + jj];
-            const float down = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x114, 0xf, 0xf, false));
-            const float up = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(other), 0x104, 0xf, 0xf, false));
-            val[jj] = mine + (upper ? down : up);  // row_shr:4 / row_shl:4
+            const float lo = val[jj] + dpp_f32<0x104>(val[jj]);                   // row_shl:4
+            const float hi = val[half + jj] + dpp_f32<0x114>(val[half + jj]);     // row_shr:4
+            val[jj] = upper ? hi : lo;
         }
     }
 }
