@@ -445,3 +445,42 @@ def test_validate_ids_finds_the_first_bad_entry(lib, case):
     assert got == want
     if case in ("good", "repeat_allowed", "max_id"):
         assert got == -1
+
+
+# ------------------------------------------------------------------ random shapes
+def _random_shape(seed: int):
+    """A seeded small shape around the kernels' boundaries: k near multiples
+    of 128 and 256 (streamed or masked Grouped, staged or per-slice Direct
+    activations), ragged n, up to 300 experts and 16 slots, both layouts,
+    padded expert strides."""
+    rng = np.random.default_rng(seed)
+    dtype = int(rng.integers(0, 3))
+    size = W.DTYPE_SIZE[dtype]
+    k = int(rng.choice([1, 7, 64, 127, 128, 129, 255, 256, 257, 384, 512, 640, 768, 1024, 1032]))
+    n = int(rng.integers(1, 300))
+    n_experts = int(rng.choice([1, 2, 5, 16, 64, 300]))
+    top_k = int(rng.integers(1, min(n_experts, 16) + 1))
+    m = int(rng.integers(1, 90))
+    layout = int(rng.integers(0, 2))
+    mult = int(rng.integers(0, 2))
+    pad = int(rng.choice([0, 0, 16, 48, 2]))
+    stride = n * k * size + pad * size
+    kind = "repeat" if mult == W.IDS_MAY_REPEAT else "random"
+    return _wl(f"rand{seed}", dtype, m, n, k, top_k, n_experts, stride=stride, layout=layout, mult=mult,
+               seed=200 + seed, ids_kind=kind)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_parity_and_bit_identity(lib, seed):
+    wl = _random_shape(seed)
+    print(f"[case] random shape {seed}: dtype={wl.dtype} m={wl.m} n={wl.n} k={wl.k} top_k={wl.top_k} "
+          f"E={wl.n_experts} layout={wl.layout} mult={wl.multiplicity} stride={wl.stride}", flush=True)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    ids = _ids(wl)
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32)), "Direct and Grouped differ"
+    assert_close(yd, _oracle_y(wl, wb, x, ids), what=wl.name)
+    assert np.array_equal(yd.view(np.uint32), canonical_matmul_id(wl, wb, x, ids).view(np.uint32))
