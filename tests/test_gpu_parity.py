@@ -484,3 +484,23 @@ def test_random_shapes_parity_and_bit_identity(lib, seed):
     assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32)), "Direct and Grouped differ"
     assert_close(yd, _oracle_y(wl, wb, x, ids), what=wl.name)
     assert np.array_equal(yd.view(np.uint32), canonical_matmul_id(wl, wb, x, ids).view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_fused_step_matches_the_three_calls(lib, seed):
+    """The one-kernel route -> Direct -> combine step on seeded small shapes
+    (staged and per-slice activations, 1 to 16 slots, up to 300 experts,
+    with and without bias and renormalisation)."""
+    rng = np.random.default_rng(500 + seed)
+    dtype = int(rng.integers(0, 3))
+    k = int(rng.choice([64, 128, 200, 256, 1000, 2048, 4096, 4104]))
+    n = int(rng.integers(1, 200))
+    n_experts = int(rng.choice([1, 8, 64, 256, 300]))
+    top_k = int(rng.integers(1, min(n_experts, 16) + 1))
+    m = int(rng.integers(1, 6))
+    layout = int(rng.integers(0, 2))
+    with_bias, renorm = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    print(f"[case] random fused {seed}: dtype={dtype} m={m} n={n} k={k} top_k={top_k} E={n_experts} "
+          f"layout={layout} bias={with_bias} renorm={renorm}", flush=True)
+    _fused_vs_three_calls(lib, _wl(f"rfused{seed}", dtype, m, n, k, top_k, n_experts, layout=layout,
+                                   seed=600 + seed), with_bias=with_bias, renormalize=renorm)
