@@ -438,10 +438,10 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
 // Streamed form, for k an even number of whole vector rounds: the
 // rounds of all the jobs one block walks are a single stream.  The loads of a
 // job's first rounds are issued while the previous job computes its last
-// ones, the next job's row indices are fetched a whole job ahead, and the
-// job table (bucket counts, offsets, first job) sits in LDS, so a block never
-// waits on a dependent chain of global reads between jobs.  Arithmetic and
-// order are those of grouped_kernel.
+// ones; the job table (bucket counts, offsets, first job), the decoded job
+// descriptors and the jobs' row-map entries are in LDS or registers, so a
+// block never waits on a global read between jobs.  Arithmetic and order are
+// those of grouped_kernel.
 template <int DT, int R, int C, int WAVES, bool W32>
 __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
                                                                        const uint32_t* __restrict__ counts,
