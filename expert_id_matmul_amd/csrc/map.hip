@@ -15,6 +15,11 @@
 //            earlier in this block.  The last term is exact and ordered: it
 //            is built from each wave's same-key lane masks and a prefix over
 //            the block's waves, so the result is deterministic.
+// Small maps (up to kMapKeyedMaxRows routed rows, with the ids read per
+// block bounded) take one launch instead: block e reads every id and
+// counts the rows with key < e (its offset) and key == e (its count) with
+// two ballots per 64 ids, then writes its own rows in ascending order.  No
+// block waits for another, and the map is the same stable sort.
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
 
@@ -147,6 +152,69 @@ __global__ __launch_bounds__(64 * kMaxMapWaves) void map_scatter_kernel(
     if (active) rows[base[key] + wcnt[wave * buckets + key] + rank] = r;
 }
 
+// One block per key e (1024 threads = 16 wavefronts).  Wavefront w owns the
+// contiguous rows [w*span, (w+1)*span), span a multiple of 64, in at most
+// kMapKeyedChunks chunks of 64; so (wavefront, chunk, lane) order is row
+// order and a running count per wavefront plus a prefix over the
+// wavefronts places every row.
+constexpr int kMapKeyedWaves = 16;
+constexpr int kMapKeyedChunks = 16;
+constexpr uint32_t kMapKeyedMaxRows = 64u * kMapKeyedWaves * kMapKeyedChunks;  // 16384
+
+__global__ __launch_bounds__(64 * kMapKeyedWaves) void map_keyed_kernel(
+    const uint32_t* __restrict__ ids, uint32_t routed_rows, uint32_t n_experts, uint32_t span,
+    uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets, uint32_t* __restrict__ rows) {
+    __shared__ uint32_t lt_s[kMapKeyedWaves], eq_s[kMapKeyedWaves];
+    const uint32_t e = blockIdx.x;  // key: an expert, or n_experts for ids naming none
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t first = (uint32_t)wave * span + (uint32_t)lane;
+    const int chunks = (int)(span >> 6);
+    // every id of this wavefront's rows first, then the two counts
+    uint32_t key[kMapKeyedChunks];
+#pragma unroll
+    for (int c = 0; c < kMapKeyedChunks; ++c) {
+        const uint32_t r = first + 64u * (uint32_t)c;
+        key[c] = c < chunks && r < routed_rows ? key_of(ids[r], n_experts) : 0xffffffffu;
+    }
+    uint32_t lt = 0, eq = 0;
+#pragma unroll
+    for (int c = 0; c < kMapKeyedChunks; ++c) {
+        lt += (uint32_t)__popcll(__ballot(key[c] < e));
+        eq += (uint32_t)__popcll(__ballot(key[c] == e));
+    }
+    if (lane == 0) {
+        lt_s[wave] = lt;
+        eq_s[wave] = eq;
+    }
+    __syncthreads();
+    uint32_t offset = 0, count = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kMapKeyedWaves; ++w) {
+        offset += lt_s[w];
+        count += eq_s[w];
+        if (w < wave) before += eq_s[w];
+    }
+    if (threadIdx.x == 0) {
+        counts[e] = count;
+        offsets[e] = offset;
+        if (e == 0) offsets[n_experts + 1] = routed_rows;
+    }
+    uint32_t pos = offset + before;
+    const uint64_t below = lanes_below(lane);
+#pragma unroll
+    for (int c = 0; c < kMapKeyedChunks; ++c) {
+        const uint64_t m = __ballot(key[c] == e);
+        if (key[c] == e) rows[pos + (uint32_t)__popcll(m & below)] = first + 64u * (uint32_t)c;
+        pos += (uint32_t)__popcll(m);
+    }
+}
+
+// the one-launch form reads all routed_rows ids in each of n_experts+1
+// blocks: kept to small maps with at most 2^24 id reads in total
+bool map_keyed_fits(uint32_t routed_rows, uint32_t n_experts) {
+    return routed_rows <= kMapKeyedMaxRows && (uint64_t)(n_experts + 1) * routed_rows <= (1ull << 24);
+}
+
 int key_bits(uint32_t n_experts) {
     int bits = 0;
     while ((1u << bits) <= n_experts) ++bits;  // keys 0..n_experts
@@ -174,6 +242,13 @@ uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts) {
 
 hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_experts,
                       const MapBuffers& buf, hipStream_t stream) {
+    if (map_keyed_fits(routed_rows, n_experts)) {
+        const uint32_t per_wave = (routed_rows + kMapKeyedWaves - 1) / kMapKeyedWaves;
+        const uint32_t span = (per_wave + 63) / 64 * 64;  // <= 64 * kMapKeyedChunks
+        hipLaunchKernelGGL(map_keyed_kernel, dim3(n_experts + 1), dim3(64 * kMapKeyedWaves), 0, stream, ids,
+                           routed_rows, n_experts, span, buf.counts, buf.offsets, buf.rows);
+        return hipGetLastError();
+    }
     const uint32_t waves = map_waves(n_experts);
     const uint32_t blocks = map_blocks(routed_rows, n_experts);
     const uint32_t buckets = n_experts + 1;

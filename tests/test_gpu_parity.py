@@ -268,7 +268,12 @@ def test_router_ties_and_raw_scores(lib):
 
 
 # ------------------------------------------------------------------ map
-@pytest.mark.parametrize("case", ["balanced", "skewed", "repeat", "random", "invalid", "large"])
+# Up to 16384 routed rows (and at most 2^24 ids read over all keys) the map is
+# one launch with a block per key; above, a histogram pass and a scatter pass.
+# "rows_16384" fills every chunk of the one-launch form; "rows_16388" and
+# "experts_2048" are just past its two limits.
+@pytest.mark.parametrize("case", ["balanced", "skewed", "repeat", "random", "invalid", "large",
+                                  "rows_16384", "rows_16388", "experts_2048"])
 def test_map_is_exact(lib, case):
     print(f"[case] map {case}", flush=True)
     if case in ("balanced", "skewed", "repeat"):
@@ -278,6 +283,11 @@ def test_map_is_exact(lib, case):
         m, top_k, E = 2048, 8, 256
         logits = W.random_f32((m, E), 70)
         ids = oracle.route(logits, None, top_k)[0]
+    elif case in ("rows_16384", "rows_16388", "experts_2048"):
+        m, top_k, E = {"rows_16384": (16384, 1, 8), "rows_16388": (4097, 4, 64),
+                       "experts_2048": (1024, 16, 2048)}[case]
+        ids = np.random.default_rng(72).integers(0, E, size=(m, top_k)).astype(np.uint32)
+        ids[7, 0] = E + 3  # one id naming no expert
     else:
         m, top_k, E = 300, 5, 37
         ids = np.random.default_rng(71).integers(0, E, size=(m, top_k)).astype(np.uint32)
