@@ -508,9 +508,16 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         __syncthreads();
     }
     const uint32_t total_jobs = job_start[buckets];
-    const uint32_t per_xcd = gridDim.x / kXcds;
-    uint32_t job = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (job >= total_jobs) return;  // the whole block leaves together
+    // Each XCD walks one contiguous eighth of the job list with its blocks
+    // side by side (block l of the XCD takes jobs first + l + i*per_xcd), so
+    // all row tiles of one (expert, column tile) meet in one L2 and the
+    // weight columns are fetched from HBM once.
+    const uint32_t per_xcd = gridDim.x / kXcds;             // blocks on one XCD
+    const uint32_t xcd_jobs = (total_jobs + kXcds - 1) / kXcds;
+    const uint32_t xcd = blockIdx.x % kXcds;
+    const uint32_t job = xcd * xcd_jobs + blockIdx.x / kXcds;  // this block's first job
+    const uint32_t job_end = min(total_jobs, (xcd + 1) * xcd_jobs);
+    if (job >= job_end) return;  // the whole block leaves together
 
     struct Job {
         uint32_t e;          // bucket (n_experts = ids naming no expert)
@@ -519,7 +526,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         uint32_t slot;       // its place in the decoded chunk (row-map entries in LDS)
         int row_count;
     };
-    // Job descriptors.  The block's jobs are job + i*gridDim.x, i = 0, 1, ...
+    // Job descriptors.  The block's jobs are job + i*per_xcd < job_end.
     // A wavefront decodes 64 of them at once, one per lane, and keeps them in
     // three registers; a job is then three lane reads, so the per-job path
     // has no dependent chain of LDS lookups.  Lane L of a chunk starting at
@@ -540,8 +547,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         d_erc = 0;
         d_col0 = 0;
         d_rb = 0;
-        const uint64_t jb64 = (uint64_t)job + ((uint64_t)i0 + (uint64_t)lane) * gridDim.x;
-        if (jb64 < total_jobs) {
+        const uint64_t jb64 = (uint64_t)job + ((uint64_t)i0 + (uint64_t)lane) * per_xcd;
+        if (jb64 < job_end) {
             const uint32_t jb = (uint32_t)jb64;
             uint32_t e = 0;
             for (uint32_t st = top; st; st >>= 1)
@@ -574,7 +581,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         }
         __syncthreads();
     };
-    // the block's job number i (job + i*gridDim.x < total_jobs)
+    // the block's job number i (job + i*per_xcd < job_end)
     auto decode = [&](uint32_t i) {
         if (i - chunk_base >= 64u) refill(i);  // block-uniform
         const int L = (int)(i - chunk_base);
@@ -719,13 +726,13 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // never copied between registers): while slot c's job runs, slot 1-c
     // holds the next job, whose row indices are already in flight.  The
     // block's job count is known up front, so the job loop has one exit.
-    const uint32_t my_jobs = (total_jobs - job + gridDim.x - 1) / gridDim.x;
+    const uint32_t my_jobs = (job_end - job + per_xcd - 1) / per_xcd;
     Job jobs[2];
     Rows rws[2];
-    uint32_t next = job + gridDim.x, next_i = 1;
+    uint32_t next = job + per_xcd, next_i = 1;
     jobs[0] = decode(0);
     rws[0] = fetch_rows(jobs[0]);
-    jobs[1] = next < total_jobs ? decode(next_i) : jobs[0];
+    jobs[1] = next < job_end ? decode(next_i) : jobs[0];
     rws[1] = fetch_rows(jobs[1]);
 
     // A step is two rounds: the weights of its rounds sit in register slots
@@ -781,9 +788,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         else if (groups > R / 4) steps(IntC<R / 2>{});
         else steps(IntC<R / 4>{});
         finish(jobs[c], rws[c]);
-        next += gridDim.x;
+        next += per_xcd;
         ++next_i;
-        jobs[c] = next < total_jobs ? decode(next_i) : jobs[o];
+        jobs[c] = next < job_end ? decode(next_i) : jobs[o];
         rws[c] = fetch_rows(jobs[c]);
     };
     uint32_t i = 0;
