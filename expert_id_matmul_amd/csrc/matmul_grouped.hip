@@ -669,27 +669,28 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
 #pragma unroll
         for (int c = 0; c < C; ++c) acc[r][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // one round from LDS tile `tile` (= 2*buffer + half) for the first RR
-    // row groups of the tile
-    auto compute_rows = [&](int tile, const float (&w)[C][kGranule], auto rr) __attribute__((always_inline)) {
-        constexpr int RR = decltype(rr)::value;
+    // one round from LDS tile `tile` (= 2*buffer + half) for row groups
+    // R0 .. R0 + R/2 - 1 of the tile (each accumulator still takes its k
+    // elements in order)
+    auto compute_rows = [&](int tile, const float (&w)[C][kGranule], auto r0) __attribute__((always_inline)) {
+        constexpr int R0 = decltype(r0)::value, RN = R / 2;
         const float* xb = xs + (size_t)tile * BM * kRoundK;
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            float2 xa[RR];
+            float2 xa[RN];
 #pragma unroll
-            for (int r = 0; r < RR; ++r) {
-                const int row = 4 * r + q;
+            for (int r = 0; r < RN; ++r) {
+                const int row = 4 * (R0 + r) + q;
                 const int chunk = swz(row, 2 * b + (pr >> 1));
                 xa[r] = *reinterpret_cast<const float2*>(xb + row * kRoundK + chunk * 4 + (pr & 1) * 2);
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int r = 0; r < RR; ++r) {
+                for (int r = 0; r < RN; ++r) {
                     const float xv = i == 0 ? xa[r].x : xa[r].y;
 #pragma unroll
-                    for (int c = 0; c < C; ++c) acc[r][c] = mfma_step(xv, w[c][2 * pr + i], acc[r][c]);
+                    for (int c = 0; c < C; ++c) acc[R0 + r][c] = mfma_step(xv, w[c][2 * pr + i], acc[R0 + r][c]);
                 }
         }
     };
@@ -752,8 +753,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // One step from LDS buffer `buf`: request the next step's activations
     // (rounds gx, gx+1 of the rows xrows), then per round widen its weights,
     // refill the slot with round gw (gw+1) of job j and compute; publish the
-    // activations to the other buffer.
-    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, auto rr) __attribute__((always_inline)) {
+    // activations to the other buffer.  `upper`: the tile has rows in its
+    // upper half of row groups (uniform).
+    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, bool upper) __attribute__((always_inline)) {
         const XTile<2 * XPER> t = load_x(xrows, gx);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -763,7 +765,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
             __builtin_amdgcn_sched_barrier(0);
             fetch_w(j, gw + h, ring[h]);
             __builtin_amdgcn_sched_barrier(0);
-            compute_rows(2 * buf + h, w, rr);
+            compute_rows(2 * buf + h, w, IntC<0>{});
+            if (upper) compute_rows(2 * buf + h, w, IntC<R / 2>{});
             __builtin_amdgcn_sched_barrier(0);
         }
         store_x(buf ^ 1, t);
@@ -775,18 +778,15 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // stay in bounds, its results unused)
     auto run_job = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value, o = 1 - c;
-        // An expert's last row tile skips the steps of its empty 4-row
-        // groups (their outputs are never stored; the others keep their
-        // order): the job runs with RR = R, R/2 or R/4 row groups.
-        auto steps = [&](auto rr) __attribute__((always_inline)) {
-            int g = 0;
-            for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, rr);
-            step(rws[o].x, 0, jobs[o], 0, rr);
-        };
-        const int groups = (jobs[c].row_count + 3) / 4;
-        if (groups > R / 2) steps(IntC<R>{});
-        else if (groups > R / 4) steps(IntC<R / 2>{});
-        else steps(IntC<R / 4>{});
+        // An expert's last row tile with at most 2R rows skips the steps of
+        // the upper half of its row groups (their outputs are never stored;
+        // the others keep their order).  One uniform branch per round does
+        // it, so every job runs the same loop: separate loops per row count
+        // cost more in register copies at their entries than they saved.
+        const bool upper = __builtin_amdgcn_readfirstlane(jobs[c].row_count) > 4 * (R / 2);
+        int g = 0;
+        for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, upper);
+        step(rws[o].x, 0, jobs[o], 0, upper);
         finish(jobs[c], rws[c]);
         next += per_xcd;
         ++next_i;
