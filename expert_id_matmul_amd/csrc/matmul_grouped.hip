@@ -27,11 +27,11 @@
 // exchange that keeps the canonical pairing (b with b^8, then b^4, b^2,
 // b^1) and leaves each lane with R*C/4 finished outputs.
 //
-// Jobs are numbered expert-major (bucket e, column tile nt, row tile mt), row
-// tile fastest; the block ids are remapped so that the blocks resident on
-// one XCD (the hardware deals blocks to the 8 XCDs round-robin) walk a
-// contiguous range of jobs and share that expert's weight columns in their
-// L2.  Each block reads the map's per-expert counts and scans them itself.
+// Jobs are numbered expert-major (bucket e, row tile mt, column tile nt),
+// column tile fastest; the block ids are remapped so that the blocks
+// resident on one XCD (the hardware deals blocks to the 8 XCDs round-robin)
+// walk a contiguous range of jobs and share that expert's weights (and a row
+// tile's activations) in their L2.  Each block reads the map's per-expert counts and scans them itself.
 // The last bucket (ids >= n_experts) gets quiet NaN rows.
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
@@ -180,7 +180,6 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
     constexpr int XCHUNKS = BM * (kRoundK / 4);          // 16-byte chunks per activation tile
     static_assert(XCHUNKS % THREADS == 0, "activation tile must split evenly");
     constexpr int XPER = XCHUNKS / THREADS;              // chunks per thread per round
-    constexpr int NP = Pieces<DT>::value;
 
     extern __shared__ __align__(16) uint8_t smem[];
     float* xs = reinterpret_cast<float*>(smem);          // [2][BM][128]
@@ -240,8 +239,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
         }
         const uint32_t e = lo;
         const uint32_t local = job - job_start[e];
-        const uint32_t mtiles = (counts[e] + BM - 1) / BM;
-        const uint32_t nt = local / mtiles, mt = local % mtiles;
+        const uint32_t mt = local / ntiles, nt = local % ntiles;
         const uint32_t row_begin = offsets[e] + mt * BM;
         const int row_count = (int)min((uint32_t)BM, counts[e] - mt * BM);
         const int col_base = (int)(nt * BN) + wave * 4 * C;
@@ -555,8 +553,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 if (e + st < buckets && job_start[e + st] <= jb) e += st;
             const uint32_t cnt = cnt_s[e];
             const uint32_t local = jb - job_start[e];
-            const uint32_t mtiles = (cnt + BM - 1) / BM;
-            const uint32_t nt = local / mtiles, mt = local - nt * mtiles;
+            const uint32_t mt = local / ntiles, nt = local - mt * ntiles;
             d_erc = e | (min((uint32_t)BM, cnt - mt * BM) << 16);
             d_col0 = nt * BN;
             d_rb = off_s[e] + mt * BM;
