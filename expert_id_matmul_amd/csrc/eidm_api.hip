@@ -226,12 +226,15 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
     return EIDM_OK;
 }
 
+// build_map = false: the id -> row map is already in buf (Grouped only)
 int run_matmul(const eidm::MatmulArgs& args, const eidm::MapBuffers& buf, int chosen,
-               hipStream_t stream) {
+               hipStream_t stream, bool build_map = true) {
     hipError_t err;
     if (chosen == EIDM_ROUTE_GROUPED) {
-        err = eidm::launch_map(args.ids, args.m * args.top_k, args.n_experts, buf, stream);
-        if (err != hipSuccess) return device_fail(err, "map launch");
+        if (build_map) {
+            err = eidm::launch_map(args.ids, args.m * args.top_k, args.n_experts, buf, stream);
+            if (err != hipSuccess) return device_fail(err, "map launch");
+        }
         err = eidm::launch_grouped(args, buf, device_cus(), stream);
         if (err != hipSuccess) return device_fail(err, "grouped launch");
     } else {
@@ -381,6 +384,34 @@ int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint
     if (route_taken) *route_taken = chosen;
     return ok();
 }
+
+}  // extern "C"
+
+namespace eidm {
+
+// The map lives at offsets of the Grouped scratch that depend only on the
+// routed-row count and the expert count, so calls over the same ids, routed
+// rows and experts with the same scratch can share one map.
+int matmul_id_shared_map(const eidm_shape* shape, int route, const void* weights, uint64_t weight_bytes,
+                         const float* input, const uint32_t* ids, float* output, void* scratch,
+                         uint64_t scratch_bytes, hipStream_t stream, bool* map_ready, int* route_taken) {
+    MatmulArgs args{};
+    MapBuffers buf{};
+    int chosen = 0;
+    int rc = prepare_matmul(shape, route, weights, weight_bytes, input, ids, output, scratch,
+                            scratch_bytes, &args, &buf, &chosen);
+    if (rc) return rc;
+    const bool grouped = chosen == EIDM_ROUTE_GROUPED;
+    rc = run_matmul(args, buf, chosen, stream, !(grouped && *map_ready));
+    if (rc) return rc;
+    if (grouped) *map_ready = true;
+    if (route_taken) *route_taken = chosen;
+    return ok();
+}
+
+}  // namespace eidm
+
+extern "C" {
 
 int eidm_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const float* gates,
                  float* out, void* stream) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "eidm.h"
+
 namespace eidm {
 
 // Largest expert count the kernels take (router state per lane, map tables).
@@ -47,6 +49,13 @@ hipError_t launch_route(const float* logits, const float* bias, uint32_t m, uint
                         hipStream_t stream);
 hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_experts,
                       const MapBuffers& buf, hipStream_t stream);
+// eidm_matmul_id for a sequence of calls over one set of ids (and one
+// scratch): a Grouped call skips the id -> row map when *map_ready says an
+// earlier Grouped call of the sequence left it in the scratch, and sets
+// *map_ready when it builds it.
+int matmul_id_shared_map(const eidm_shape* shape, int route, const void* weights, uint64_t weight_bytes,
+                         const float* input, const uint32_t* ids, float* output, void* scratch,
+                         uint64_t scratch_bytes, hipStream_t stream, bool* map_ready, int* route_taken);
 hipError_t launch_direct(const MatmulArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                           hipStream_t stream);

@@ -158,10 +158,17 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
 
     rc = eidm_route_topk(logits, bias, shape->m, shape->n_experts, shape->top_k, renormalize, ids, gates, stream);
     if (rc) return rc;
+    // the three projections share the ids, routed rows and experts: the
+    // first Grouped one builds the id -> row map in the scratch, the others
+    // reuse it
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bool map_ready = false;
     int taken = 0;
-    rc = eidm_matmul_id(&gu, route, w_gate, gate_up_bytes, x, ids, g, grouped, l.grouped_bytes, stream, &taken);
+    rc = eidm::matmul_id_shared_map(&gu, route, w_gate, gate_up_bytes, x, ids, g, grouped, l.grouped_bytes, st,
+                                    &map_ready, &taken);
     if (rc) return rc;
-    rc = eidm_matmul_id(&gu, route, w_up, gate_up_bytes, x, ids, u, grouped, l.grouped_bytes, stream, nullptr);
+    rc = eidm::matmul_id_shared_map(&gu, route, w_up, gate_up_bytes, x, ids, u, grouped, l.grouped_bytes, st,
+                                    &map_ready, nullptr);
     if (rc) return rc;
     const uint64_t count = (uint64_t)shape->m * shape->top_k * shape->inter;
     uint64_t blocks = (count / 4 + 255) / 256;
@@ -171,7 +178,8 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
                        static_cast<hipStream_t>(stream), g, u, count);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return api_fail(EIDM_E_DEVICE, "silu * up launch: %s", hipGetErrorString(err));
-    rc = eidm_matmul_id(&dn, route, w_down, down_bytes, g, ids, y, grouped, l.grouped_bytes, stream, nullptr);
+    rc = eidm::matmul_id_shared_map(&dn, route, w_down, down_bytes, g, ids, y, grouped, l.grouped_bytes, st,
+                                    &map_ready, nullptr);
     if (rc) return rc;
     rc = eidm_combine(shape->m, shape->top_k, shape->hidden, y, gates, out, stream);
     if (rc) return rc;
