@@ -368,7 +368,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the expert-ID matmul path here has no multi-GPU "
-              "form (sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "form (expert or column sharding is a design, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_calibration:
