@@ -170,9 +170,11 @@ int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t
  *   rows    device u32 [m*top_k]: the rows, grouped by key, ascending
  *           within each key
  *   scratch device, >= eidm_map_scratch_bytes(m, top_k, n_experts) bytes,
- *           4-byte aligned (per-block histograms)
- * Results are exact and deterministic.  Requires m*top_k < 2^31 and
- * n_experts <= 2048.
+ *           4-byte aligned (per-block histograms; small maps, up to 16384
+ *           routed rows, are built in one pass without it, but the size is
+ *           required either way)
+ * Results are exact and deterministic, the same for either form.  Requires
+ * m*top_k < 2^31 and n_experts <= 2048.
  */
 int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
              uint32_t* counts, uint32_t* offsets, uint32_t* rows, void* scratch,
