@@ -433,14 +433,15 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
     }
 }
 
-// Streamed form, for k an even number of whole vector rounds: the
-// rounds of all the jobs one block walks are a single stream.  The loads of a
-// job's first rounds are issued while the previous job computes its last
-// ones; the job table (bucket counts, offsets, first job), the decoded job
-// descriptors and the jobs' row-map entries are in LDS or registers, so a
-// block never waits on a global read between jobs.  Arithmetic and order are
-// those of grouped_kernel.
-template <int DT, int R, int C, int WAVES, bool W32>
+// Streamed form, for k a whole number of vector rounds (at least two, at
+// least three when odd): the rounds of all the jobs one block walks are a
+// single stream.  The loads of a job's first rounds are issued while the
+// previous job computes its last ones; the job table (bucket counts, offsets,
+// first job), the decoded job descriptors and the jobs' row-map entries are
+// in LDS or registers, so a block never waits on a global read between jobs.
+// Arithmetic and order are those of grouped_kernel.  ODD: the number of
+// rounds is odd (see run_job).
+template <int DT, int R, int C, int WAVES, bool W32, bool ODD>
 __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
                                                                        const uint32_t* __restrict__ counts,
                                                                        const uint32_t* __restrict__ offsets,
@@ -613,16 +614,18 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     };
 
     const uint32_t x_div = a.layout == 1 ? 1u : a.top_k;  // routed row -> activation row
-    // this thread's chunks of the activation tiles of rounds g and g+1
-    auto load_x = [&](const uint32_t (&routed)[XPER], int g) {
+    // this thread's chunks of the activation tiles of two rounds: round g0
+    // of the rows r0 (half 0) and round g1 of the rows r1 (half 1)
+    auto load_x = [&](const uint32_t (&r0)[XPER], int g0, const uint32_t (&r1)[XPER], int g1) {
         XTile<2 * XPER> t;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int jj = 0; jj < XPER; ++jj) {
                 const int chunk = (tid + jj * THREADS) & 31;
-                const uint32_t xr = routed[jj] / x_div;
-                t.v[h * XPER + jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + (g + h) * kRoundK + chunk * 4);
+                const uint32_t xr = (h == 0 ? r0[jj] : r1[jj]) / x_div;
+                const int g = h == 0 ? g0 : g1;
+                t.v[h * XPER + jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + g * kRoundK + chunk * 4);
             }
         return t;
     };
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     WeightRound<DT, C> ring[2];
     int buf = 0;
     {
-        const XTile<2 * XPER> t = load_x(rws[0].x, 0);
+        const XTile<2 * XPER> t = load_x(rws[0].x, 0, rws[0].x, 1);
         fetch_w(jobs[0], 0, ring[0]);
         fetch_w(jobs[0], 1, ring[1]);
         store_x(0, t);
@@ -748,31 +751,46 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     __syncthreads();
 
     // One step from LDS buffer `buf`: request the next step's activations
-    // (rounds gx, gx+1 of the rows xrows), then per round widen its weights,
-    // refill the slot with round gw (gw+1) of job j and compute; publish the
-    // activations to the other buffer.  `upper`: the tile has rows in its
-    // upper half of row groups (uniform).
-    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, bool upper) __attribute__((always_inline)) {
-        const XTile<2 * XPER> t = load_x(xrows, gx);
+    // (round gx0 of the rows xr0, round gx1 of the rows xr1), then per round
+    // h widen its weights, refill slot h with round gw0 of job j0 (h = 0) or
+    // gw1 of job j1 (h = 1) and compute; publish the activations to the other
+    // buffer.  up0, up1: the tile of round h has rows in its upper half of
+    // row groups (uniform).  mid() runs between the two rounds.
+    auto step2 = [&](const uint32_t (&xr0)[XPER], int gx0, const uint32_t (&xr1)[XPER], int gx1,
+                     const Job& j0, int gw0, const Job& j1, int gw1, bool up0, bool up1,
+                     auto mid) __attribute__((always_inline)) {
+        const XTile<2 * XPER> t = load_x(xr0, gx0, xr1, gx1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float w[C][kGranule];
             widen_w_pieces_all<DT, C>(ring[h], w);
             __builtin_amdgcn_sched_barrier(0);
-            fetch_w(j, gw + h, ring[h]);
+            fetch_w(h == 0 ? j0 : j1, h == 0 ? gw0 : gw1, ring[h]);
             __builtin_amdgcn_sched_barrier(0);
             compute_rows(2 * buf + h, w, IntC<0>{});
-            if (upper) compute_rows(2 * buf + h, w, IntC<R / 2>{});
+            if (h == 0 ? up0 : up1) compute_rows(2 * buf + h, w, IntC<R / 2>{});
             __builtin_amdgcn_sched_barrier(0);
+            if (h == 0) {
+                mid();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         store_x(buf ^ 1, t);
         __syncthreads();
         buf ^= 1;
     };
-    // the job in slot c (rounds is even); afterwards slot c takes the job
-    // after next (or repeats slot 1-c's job when there is none: its loads
-    // stay in bounds, its results unused)
+    // the usual step: rounds gx, gx+1 of the rows xrows, rounds gw, gw+1 of job j
+    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, bool upper) __attribute__((always_inline)) {
+        step2(xrows, gx, xrows, gx + 1, j, gw, j, gw + 1, upper, upper, [] {});
+    };
+    // the job in slot c; afterwards slot c takes the job after next (or
+    // repeats slot 1-c's job when there is none: its loads stay in bounds,
+    // its results unused).  With an even number of rounds every job starts
+    // on a step.  With an odd number (at least three) the jobs of slot 0
+    // start on a step and the jobs of slot 1 one round later: a slot-0 job's
+    // last round and the next job's first share a step, with the slot-0 job
+    // finished between them, so the stream of steps has no gap.
     auto run_job = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value, o = 1 - c;
         // An expert's last row tile with at most 2R rows skips the steps of
@@ -781,10 +799,29 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         // it, so every job runs the same loop: separate loops per row count
         // cost more in register copies at their entries than they saved.
         const bool upper = __builtin_amdgcn_readfirstlane(jobs[c].row_count) > 4 * (R / 2);
-        int g = 0;
-        for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, upper);
-        step(rws[o].x, 0, jobs[o], 0, upper);
-        finish(jobs[c], rws[c]);
+        if constexpr (!ODD) {
+            int g = 0;
+            for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, upper);
+            step(rws[o].x, 0, jobs[o], 0, upper);
+            finish(jobs[c], rws[c]);
+        } else if constexpr (c == 0) {
+            // rounds 0 .. rounds-2 in pairs; the last pair requests this
+            // job's last round and slot 1's first
+            int g = 0;
+            for (; g + 3 < rounds; g += 2) step(rws[0].x, g + 2, jobs[0], g + 2, upper);
+            step2(rws[0].x, rounds - 1, rws[1].x, 0, jobs[0], rounds - 1, jobs[1], 0, upper, upper, [] {});
+            // the shared step: this job's last round, then slot 1's round 0
+            const bool upper1 = __builtin_amdgcn_readfirstlane(jobs[1].row_count) > 4 * (R / 2);
+            step2(rws[1].x, 1, rws[1].x, 2, jobs[1], 1, jobs[1], 2, upper, upper1,
+                  [&] { finish(jobs[0], rws[0]); });
+        } else {
+            // round 0 is done: rounds 1 .. rounds-1 in pairs, the last one
+            // requesting slot 0's first two
+            int g = 1;
+            for (; g + 3 < rounds; g += 2) step(rws[1].x, g + 2, jobs[1], g + 2, upper);
+            step(rws[0].x, 0, jobs[0], 0, upper);
+            finish(jobs[1], rws[1]);
+        }
         next += per_xcd;
         ++next_i;
         jobs[c] = next < job_end ? decode(next_i) : jobs[o];
@@ -806,12 +843,17 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const uint64_t ntiles = (a.n + BN - 1) / BN;
     // every bucket adds at most one partial row tile
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
-    // the streamed form needs an even number of whole vector rounds
-    const bool stream_form = a.vec && a.k % (2 * kRoundK) == 0;
+    // the streamed form needs whole vector rounds: two or more, three or
+    // more when their number is odd
+    const uint32_t rounds = a.k / kRoundK;
+    const bool odd = rounds % 2 == 1;
+    const bool stream_form = a.vec && a.k % kRoundK == 0 && rounds >= (odd ? 3u : 2u);
     const bool w32 = (uint64_t)a.n * a.k * DtypeSize<DT>::value + 256 <= 0xffffffffull;
     auto kernel = !stream_form ? grouped_kernel<DT, R, C, WAVES>
-                  : w32        ? grouped_stream_kernel<DT, R, C, WAVES, true>
-                               : grouped_stream_kernel<DT, R, C, WAVES, false>;
+                  : odd        ? (w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, true>
+                                      : grouped_stream_kernel<DT, R, C, WAVES, false, true>)
+                               : (w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, false>
+                                      : grouped_stream_kernel<DT, R, C, WAVES, false, false>);
     const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4 + 64 * BM) : (a.n_experts + 2);
     const size_t lds = (stream_form ? 4 : 2) * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;

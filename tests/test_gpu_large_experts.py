@@ -21,7 +21,6 @@ from helpers import TOL, canonical_matmul_id, check_guarded, ids_to_dev, poisone
 
 pytestmark = pytest.mark.gpu
 
-K = 8192            # k % 256 == 0: the Grouped kernel streams its rounds
 EXTRA_COLUMNS = 40  # n * k * size exceeds 4 GiB by 40 rows
 
 
@@ -31,8 +30,11 @@ def _small_wl(dtype, k):
                       0, 0.0, "random", "softmax")
 
 
-@pytest.mark.parametrize("dtype", [W.DT_BF16, W.DT_F32], ids=lambda d: W.DTYPE_NAME[d])
-def test_experts_larger_than_4_gib(lib, dtype):
+# k a whole number of 128-element rounds, so the Grouped kernel streams its
+# rounds: 64 of them, and 63 (an odd number: jobs start on alternate rounds)
+@pytest.mark.parametrize("dtype,K", [(W.DT_BF16, 8192), (W.DT_F32, 8192), (W.DT_BF16, 8064)],
+                         ids=["bf16", "f32", "bf16_odd_rounds"])
+def test_experts_larger_than_4_gib(lib, dtype, K):
     torch.cuda.set_device(0)
     size = W.DTYPE_SIZE[dtype]
     n = (1 << 32) // (K * size) + EXTRA_COLUMNS

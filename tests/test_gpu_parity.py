@@ -61,12 +61,20 @@ SMALL = [
     # in LDS: Direct reads it per slice from memory
     _wl("vec_bf16_long_k", W.DT_BF16, 3, 40, 4224, 4, 8, seed=38),
     _wl("may_repeat", W.DT_BF16, 12, 48, 256, 5, 3, mult=W.IDS_MAY_REPEAT, seed=37, ids_kind="repeat"),
-    # k an even number of whole 128-element rounds: Grouped streams the rounds
-    # of consecutive jobs; these give blocks several jobs each, in odd and
-    # even numbers, with a ragged last column tile
+    # k a whole number of 128-element rounds: Grouped streams the rounds of
+    # consecutive jobs; these give blocks several jobs each, in odd and even
+    # numbers, with a ragged last column tile
     _wl("stream_bf16_jobs", W.DT_BF16, 256, 1000, 512, 8, 16, seed=60),
     _wl("stream_f16_slot", W.DT_F16, 150, 700, 256, 6, 10, layout=W.LAYOUT_SLOTTED, seed=61),
     _wl("stream_f32", W.DT_F32, 128, 2000, 256, 4, 8, seed=62),
+    # an odd number of rounds (3 and 5): jobs alternate between starting on a
+    # step and one round later, one step holding two jobs' rounds; blocks of
+    # 4 or 5 jobs, 1 or 2 and 3, last row tiles with and without
+    # rows in the upper half of the tile (k = 384, 640)
+    _wl("stream_odd_bf16_jobs", W.DT_BF16, 256, 1000, 384, 8, 16, seed=63),
+    _wl("stream_odd_bf16_five", W.DT_BF16, 300, 1000, 640, 8, 16, seed=64),
+    _wl("stream_odd_f16_slot", W.DT_F16, 150, 700, 384, 6, 10, layout=W.LAYOUT_SLOTTED, seed=65),
+    _wl("stream_odd_f32", W.DT_F32, 150, 2000, 384, 4, 8, seed=66),
 ]
 
 
@@ -152,7 +160,7 @@ def _plant(rng, bits: np.ndarray, special: np.ndarray, frac: float) -> np.ndarra
 
 
 @pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_F16, W.DT_BF16], ids=["f32", "f16", "bf16"])
-@pytest.mark.parametrize("k", [512, 300], ids=["streamed", "masked"])
+@pytest.mark.parametrize("k", [512, 384, 300], ids=["streamed", "streamed_odd", "masked"])
 def test_bit_identity_with_special_values(lib, dtype, k):
     """Subnormal, signed-zero, infinite, NaN and extreme weights and activations:
     Direct and Grouped give the same bits (NaN for NaN), and so does the CPU
@@ -198,7 +206,8 @@ def test_modular_fill_weights(lib):
     assert_close(yd, _oracle_y(wl, wb, x, ids))
 
 
-@pytest.mark.parametrize("m,n,k", [(10, 40, 200), (200, 640, 512)], ids=["masked", "streamed"])
+@pytest.mark.parametrize("m,n,k", [(10, 40, 200), (200, 640, 512), (200, 640, 384)],
+                         ids=["masked", "streamed", "streamed_odd"])
 def test_ids_naming_no_expert_give_nan_rows_in_both_routes(lib, m, n, k):
     print(f"[case] bad ids m={m} n={n} k={k}", flush=True)
     wl = _wl("bad_ids", W.DT_BF16, m, n, k, 3, 6, seed=50)
