@@ -433,15 +433,22 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
     }
 }
 
-// Streamed form, for k a whole number of vector rounds (at least two, at
-// least three when odd): the rounds of all the jobs one block walks are a
-// single stream.  The loads of a job's first rounds are issued while the
+// Streamed form, for vector rows (16-byte aligned, k a multiple of 4) of at
+// least two rounds (at least three when their number is odd): the rounds of
+// all the jobs one block walks are a single stream.  The loads of a job's first rounds are issued while the
 // previous job computes its last ones; the job table (bucket counts, offsets,
 // first job), the decoded job descriptors and the jobs' row-map entries are
 // in LDS or registers, so a block never waits on a global read between jobs.
 // Arithmetic and order are those of grouped_kernel.  ODD: the number of
-// rounds is odd (see run_job).
-template <int DT, int R, int C, int WAVES, bool W32, bool ODD>
+// rounds is odd (see run_job).  TAIL: k is not a multiple of 128, so the last
+// round is partly past k.  Every 16-byte weight piece and 4-element
+// activation chunk lies wholly before or past k (rows are whole 16-byte
+// pieces); those past k enter as +0, as the documented order has it.  They
+// are loaded from the same place one round earlier (in bounds, no branch
+// around the load) and replaced by zeros where they are used: activations
+// when stored to LDS, weights in the step that computes the job's last
+// round (known at each call site).
+template <int DT, int R, int C, int WAVES, bool W32, bool ODD, bool TAIL>
 __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
                                                                        const uint32_t* __restrict__ counts,
                                                                        const uint32_t* __restrict__ offsets,
@@ -469,7 +476,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     const int b = lane >> 2, q = lane & 3;
     const uint32_t ntiles = (a.n + BN - 1) / BN;
     const int n = (int)a.n, k = (int)a.k;
-    const int rounds = k / kRoundK;
+    const int rounds = TAIL ? (k + kRoundK - 1) / kRoundK : k / kRoundK;
+    const int last = rounds - 1;
+    const int tail = k - last * kRoundK;  // elements of the last round inside k (TAIL)
 
     // job table: jobs per bucket -> exclusive prefix, with counts and offsets
     {
@@ -625,12 +634,14 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 const int chunk = (tid + jj * THREADS) & 31;
                 const uint32_t xr = (h == 0 ? r0[jj] : r1[jj]) / x_div;
                 const int g = h == 0 ? g0 : g1;
-                t.v[h * XPER + jj] = *reinterpret_cast<const f32x4*>(a.input + (size_t)xr * a.k + g * kRoundK + chunk * 4);
+                const float* src = a.input + (size_t)xr * a.k + g * kRoundK + chunk * 4;
+                if constexpr (TAIL) src -= g == last && chunk * 4 >= tail ? kRoundK : 0;  // zeroed in store_x
+                t.v[h * XPER + jj] = *reinterpret_cast<const f32x4*>(src);
             }
         return t;
     };
-    // publish them to LDS buffer `buf` (rounds in halves 0 and 1)
-    auto store_x = [&](int buf, const XTile<2 * XPER>& t) {
+    // publish them to LDS buffer `buf` (rounds g0, g1 in halves 0 and 1)
+    auto store_x = [&](int buf, const XTile<2 * XPER>& t, int g0, int g1) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -638,7 +649,10 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 const int id = tid + jj * THREADS;
                 const int lr = id >> 5, chunk = id & 31;
                 float* dst = xs + ((size_t)(2 * buf + h) * BM + lr) * kRoundK + swz(lr, chunk) * 4;
-                *reinterpret_cast<f32x4*>(dst) = t.v[h * XPER + jj];
+                f32x4 v = t.v[h * XPER + jj];
+                if constexpr (TAIL)
+                    if ((h == 0 ? g0 : g1) == last && chunk * 4 >= tail) v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                *reinterpret_cast<f32x4*>(dst) = v;
             }
     };
     // this lane's weight granules of round g (columns past n read column n-1)
@@ -646,6 +660,8 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // block-uniform base (expert and round, in scalar registers) plus a
     // 32-bit lane offset fixed for the job, so the steady loop spends no
     // vector instructions on 64-bit addresses.
+    // piece i of this lane lies past k in the last round (TAIL)
+    auto w_past = [&](int i) { return b * kGranule + i * (16 / S) >= tail; };
     auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
         const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)j.wexp * a.stride;
 #pragma unroll
@@ -655,8 +671,19 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 const uint8_t* rb = base + (size_t)g * kRoundK * S;
                 const uint32_t off = (uint32_t)col * (uint32_t)a.k * (uint32_t)S + (uint32_t)(b * kGranule * S);
 #pragma unroll
-                for (int i = 0; i < Pieces<DT>::value; ++i)
-                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(rb + off + 16u * (uint32_t)i);
+                for (int i = 0; i < Pieces<DT>::value; ++i) {
+                    const uint8_t* src = rb + off + 16u * (uint32_t)i;
+                    if constexpr (TAIL) src -= g == last && w_past(i) ? kRoundK * S : 0;  // zeroed in step2
+                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(src);
+                }
+            } else if constexpr (TAIL) {
+                const uint8_t* row = base + (size_t)col * a.k * S;
+#pragma unroll
+                for (int i = 0; i < Pieces<DT>::value; ++i) {
+                    int e = g * kRoundK + b * kGranule + i * (16 / S);
+                    e -= g == last && w_past(i) ? kRoundK : 0;  // zeroed in step2
+                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(row + (size_t)e * S);
+                }
             } else {
                 load_w_pieces<DT>(base + (size_t)col * a.k * S, g * kRoundK + b * kGranule, wr.p[c]);
             }
@@ -746,7 +773,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         const XTile<2 * XPER> t = load_x(rws[0].x, 0, rws[0].x, 1);
         fetch_w(jobs[0], 0, ring[0]);
         fetch_w(jobs[0], 1, ring[1]);
-        store_x(0, t);
+        store_x(0, t, 0, 1);
     }
     __syncthreads();
 
@@ -755,14 +782,23 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // h widen its weights, refill slot h with round gw0 of job j0 (h = 0) or
     // gw1 of job j1 (h = 1) and compute; publish the activations to the other
     // buffer.  up0, up1: the tile of round h has rows in its upper half of
-    // row groups (uniform).  mid() runs between the two rounds.
+    // row groups (uniform).  mid() runs between the two rounds.  LAST (bit h):
+    // round h is its job's last round (TAIL: its pieces past k become zeros).
     auto step2 = [&](const uint32_t (&xr0)[XPER], int gx0, const uint32_t (&xr1)[XPER], int gx1,
                      const Job& j0, int gw0, const Job& j1, int gw1, bool up0, bool up1,
-                     auto mid) __attribute__((always_inline)) {
+                     auto mid, auto lastc) __attribute__((always_inline)) {
+        constexpr int LAST = decltype(lastc)::value;
         const XTile<2 * XPER> t = load_x(xr0, gx0, xr1, gx1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if (TAIL && ((LAST >> h) & 1)) {  // h is a constant after unrolling
+#pragma unroll
+                for (int c = 0; c < C; ++c)
+#pragma unroll
+                    for (int i = 0; i < Pieces<DT>::value; ++i)
+                        if (w_past(i)) ring[h].p[c][i] = u32x4{0u, 0u, 0u, 0u};
+            }
             float w[C][kGranule];
             widen_w_pieces_all<DT, C>(ring[h], w);
             __builtin_amdgcn_sched_barrier(0);
@@ -776,13 +812,15 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        store_x(buf ^ 1, t);
+        store_x(buf ^ 1, t, gx0, gx1);
         __syncthreads();
         buf ^= 1;
     };
-    // the usual step: rounds gx, gx+1 of the rows xrows, rounds gw, gw+1 of job j
-    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, bool upper) __attribute__((always_inline)) {
-        step2(xrows, gx, xrows, gx + 1, j, gw, j, gw + 1, upper, upper, [] {});
+    // the usual step: rounds gx, gx+1 of the rows xrows, rounds gw, gw+1 of
+    // job j (LAST as in step2)
+    auto step = [&](const uint32_t (&xrows)[XPER], int gx, const Job& j, int gw, bool upper,
+                    auto lastc) __attribute__((always_inline)) {
+        step2(xrows, gx, xrows, gx + 1, j, gw, j, gw + 1, upper, upper, [] {}, lastc);
     };
     // the job in slot c; afterwards slot c takes the job after next (or
     // repeats slot 1-c's job when there is none: its loads stay in bounds,
@@ -793,6 +831,9 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     // finished between them, so the stream of steps has no gap.
     auto run_job = [&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value, o = 1 - c;
+        // LAST flags for the steps holding a job's last round (only TAIL uses
+        // them; without a tail every step is the same instantiation)
+        constexpr int kLast0 = TAIL ? 1 : 0, kLast1 = TAIL ? 2 : 0;
         // An expert's last row tile with at most 2R rows skips the steps of
         // the upper half of its row groups (their outputs are never stored;
         // the others keep their order).  One uniform branch per round does
@@ -801,25 +842,26 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
         const bool upper = __builtin_amdgcn_readfirstlane(jobs[c].row_count) > 4 * (R / 2);
         if constexpr (!ODD) {
             int g = 0;
-            for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, upper);
-            step(rws[o].x, 0, jobs[o], 0, upper);
+            for (; g + 2 < rounds; g += 2) step(rws[c].x, g + 2, jobs[c], g + 2, upper, IntC<0>{});
+            step(rws[o].x, 0, jobs[o], 0, upper, IntC<kLast1>{});
             finish(jobs[c], rws[c]);
         } else if constexpr (c == 0) {
             // rounds 0 .. rounds-2 in pairs; the last pair requests this
             // job's last round and slot 1's first
             int g = 0;
-            for (; g + 3 < rounds; g += 2) step(rws[0].x, g + 2, jobs[0], g + 2, upper);
-            step2(rws[0].x, rounds - 1, rws[1].x, 0, jobs[0], rounds - 1, jobs[1], 0, upper, upper, [] {});
+            for (; g + 3 < rounds; g += 2) step(rws[0].x, g + 2, jobs[0], g + 2, upper, IntC<0>{});
+            step2(rws[0].x, rounds - 1, rws[1].x, 0, jobs[0], rounds - 1, jobs[1], 0, upper, upper, [] {},
+                  IntC<0>{});
             // the shared step: this job's last round, then slot 1's round 0
             const bool upper1 = __builtin_amdgcn_readfirstlane(jobs[1].row_count) > 4 * (R / 2);
             step2(rws[1].x, 1, rws[1].x, 2, jobs[1], 1, jobs[1], 2, upper, upper1,
-                  [&] { finish(jobs[0], rws[0]); });
+                  [&] { finish(jobs[0], rws[0]); }, IntC<kLast0>{});
         } else {
             // round 0 is done: rounds 1 .. rounds-1 in pairs, the last one
             // requesting slot 0's first two
             int g = 1;
-            for (; g + 3 < rounds; g += 2) step(rws[1].x, g + 2, jobs[1], g + 2, upper);
-            step(rws[0].x, 0, jobs[0], 0, upper);
+            for (; g + 3 < rounds; g += 2) step(rws[1].x, g + 2, jobs[1], g + 2, upper, IntC<0>{});
+            step(rws[0].x, 0, jobs[0], 0, upper, IntC<kLast1>{});
             finish(jobs[1], rws[1]);
         }
         next += per_xcd;
@@ -835,6 +877,12 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     if (i < my_jobs) run_job(IntC<0>{});
 }
 
+template <int DT, int R, int C, int WAVES, bool ODD, bool TAIL>
+auto stream_kernel(bool w32) {
+    return w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, ODD, TAIL>
+               : grouped_stream_kernel<DT, R, C, WAVES, false, ODD, TAIL>;
+}
+
 template <int DT, int R, int C, int WAVES>
 hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                       hipStream_t stream) {
@@ -843,17 +891,17 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const uint64_t ntiles = (a.n + BN - 1) / BN;
     // every bucket adds at most one partial row tile
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
-    // the streamed form needs whole vector rounds: two or more, three or
-    // more when their number is odd
-    const uint32_t rounds = a.k / kRoundK;
-    const bool odd = rounds % 2 == 1;
-    const bool stream_form = a.vec && a.k % kRoundK == 0 && rounds >= (odd ? 3u : 2u);
+    // the streamed form needs vector rows and two or more rounds (three or
+    // more when their number is odd)
+    const uint32_t rounds = (a.k + kRoundK - 1) / kRoundK;
+    const bool odd = rounds % 2 == 1, tail = a.k % kRoundK != 0;
+    const bool stream_form = a.vec && rounds >= (odd ? 3u : 2u);
     const bool w32 = (uint64_t)a.n * a.k * DtypeSize<DT>::value + 256 <= 0xffffffffull;
     auto kernel = !stream_form ? grouped_kernel<DT, R, C, WAVES>
-                  : odd        ? (w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, true>
-                                      : grouped_stream_kernel<DT, R, C, WAVES, false, true>)
-                               : (w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, false>
-                                      : grouped_stream_kernel<DT, R, C, WAVES, false, false>);
+                  : odd ? (tail ? stream_kernel<DT, R, C, WAVES, true, true>(w32)
+                                : stream_kernel<DT, R, C, WAVES, true, false>(w32))
+                        : (tail ? stream_kernel<DT, R, C, WAVES, false, true>(w32)
+                                : stream_kernel<DT, R, C, WAVES, false, false>(w32));
     const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4 + 64 * BM) : (a.n_experts + 2);
     const size_t lds = (stream_form ? 4 : 2) * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;

@@ -30,10 +30,10 @@ def _small_wl(dtype, k):
                       0, 0.0, "random", "softmax")
 
 
-# k a whole number of 128-element rounds, so the Grouped kernel streams its
-# rounds: 64 of them, and 63 (an odd number: jobs start on alternate rounds)
-@pytest.mark.parametrize("dtype,K", [(W.DT_BF16, 8192), (W.DT_F32, 8192), (W.DT_BF16, 8064)],
-                         ids=["bf16", "f32", "bf16_odd_rounds"])
+# The Grouped kernel streams the rounds: 64 of them, 63 (an odd number: jobs
+# start on alternate rounds), and 63 with the last one partly past k
+@pytest.mark.parametrize("dtype,K", [(W.DT_BF16, 8192), (W.DT_F32, 8192), (W.DT_BF16, 8064), (W.DT_BF16, 7944)],
+                         ids=["bf16", "f32", "bf16_odd_rounds", "bf16_odd_rounds_tail"])
 def test_experts_larger_than_4_gib(lib, dtype, K):
     torch.cuda.set_device(0)
     size = W.DTYPE_SIZE[dtype]

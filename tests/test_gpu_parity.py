@@ -75,6 +75,14 @@ SMALL = [
     _wl("stream_odd_bf16_five", W.DT_BF16, 300, 1000, 640, 8, 16, seed=64),
     _wl("stream_odd_f16_slot", W.DT_F16, 150, 700, 384, 6, 10, layout=W.LAYOUT_SLOTTED, seed=65),
     _wl("stream_odd_f32", W.DT_F32, 150, 2000, 384, 4, 8, seed=66),
+    # k past the last whole round (rows still whole 16-byte pieces): the last
+    # round's pieces past k enter as zeros; even and odd round counts, f32
+    # granules half inside k (k = 300, 132)
+    _wl("stream_tail_bf16_jobs", W.DT_BF16, 256, 1000, 1000, 8, 16, seed=67),
+    _wl("stream_tail_odd_bf16", W.DT_BF16, 300, 1000, 1064, 8, 16, seed=68),
+    _wl("stream_tail_f16_slot", W.DT_F16, 150, 700, 2880, 6, 10, layout=W.LAYOUT_SLOTTED, seed=69),
+    _wl("stream_tail_f32", W.DT_F32, 150, 2000, 300, 4, 8, seed=70),
+    _wl("stream_tail_f32_two_rounds", W.DT_F32, 128, 2000, 132, 4, 8, seed=71),
 ]
 
 
@@ -160,7 +168,7 @@ def _plant(rng, bits: np.ndarray, special: np.ndarray, frac: float) -> np.ndarra
 
 
 @pytest.mark.parametrize("dtype", [W.DT_F32, W.DT_F16, W.DT_BF16], ids=["f32", "f16", "bf16"])
-@pytest.mark.parametrize("k", [512, 384, 300], ids=["streamed", "streamed_odd", "masked"])
+@pytest.mark.parametrize("k", [512, 384, 1064, 300], ids=["streamed", "streamed_odd", "streamed_tail", "k300"])
 def test_bit_identity_with_special_values(lib, dtype, k):
     """Subnormal, signed-zero, infinite, NaN and extreme weights and activations:
     Direct and Grouped give the same bits (NaN for NaN), and so does the CPU
@@ -206,8 +214,8 @@ def test_modular_fill_weights(lib):
     assert_close(yd, _oracle_y(wl, wb, x, ids))
 
 
-@pytest.mark.parametrize("m,n,k", [(10, 40, 200), (200, 640, 512), (200, 640, 384)],
-                         ids=["masked", "streamed", "streamed_odd"])
+@pytest.mark.parametrize("m,n,k", [(10, 40, 200), (200, 640, 512), (200, 640, 384), (200, 640, 1000)],
+                         ids=["short", "streamed", "streamed_odd", "streamed_tail"])
 def test_ids_naming_no_expert_give_nan_rows_in_both_routes(lib, m, n, k):
     print(f"[case] bad ids m={m} n={n} k={k}", flush=True)
     wl = _wl("bad_ids", W.DT_BF16, m, n, k, 3, 6, seed=50)
