@@ -14,7 +14,9 @@ pytestmark = pytest.mark.gpu
 SMALL = [W.FfnWorkload("ffn_bf16", W.DT_BF16, 37, 96, 72, 4, 12, 51, 0.05),
          W.FfnWorkload("ffn_f16_ragged", W.DT_F16, 23, 130, 61, 3, 9, 52, 0.05),
          W.FfnWorkload("ffn_f32", W.DT_F32, 16, 64, 48, 2, 6, 53, 0.1),
-         W.FfnWorkload("ffn_many_rows", W.DT_BF16, 200, 256, 256, 8, 16, 54, 0.03)]
+         W.FfnWorkload("ffn_many_rows", W.DT_BF16, 200, 256, 256, 8, 16, 54, 0.03),
+         # gate/up k = 2880 (23 rounds, the last partly past k), down k = 1408 (11 rounds)
+         W.FfnWorkload("ffn_odd_rounds_tail", W.DT_BF16, 64, 2880, 1408, 4, 8, 55, 0.02)]
 
 
 def _device_weights(fw):
