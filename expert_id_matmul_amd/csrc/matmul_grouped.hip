@@ -435,11 +435,12 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
 
 // Streamed form, for vector rows (16-byte aligned, k a multiple of 4) of at
 // least two rounds (at least three when their number is odd): the rounds of
-// all the jobs one block walks are a single stream.  The loads of a job's first rounds are issued while the
-// previous job computes its last ones; the job table (bucket counts, offsets,
-// first job), the decoded job descriptors and the jobs' row-map entries are
-// in LDS or registers, so a block never waits on a global read between jobs.
-// Arithmetic and order are those of grouped_kernel.  ODD: the number of
+// all the jobs one block walks are a single stream.  The loads of a job's
+// first rounds are issued while the previous job computes its last ones; the
+// job table (bucket counts, offsets, first job), the decoded job descriptors
+// and the jobs' row-map entries are in LDS or registers, so a block never
+// waits on a global read between jobs.  Arithmetic and order are those of
+// grouped_kernel.  ODD: the number of
 // rounds is odd (see run_job).  TAIL: k is not a multiple of 128, so the last
 // round is partly past k.  Every 16-byte weight piece and 4-element
 // activation chunk lies wholly before or past k (rows are whole 16-byte
@@ -655,13 +656,13 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
                 *reinterpret_cast<f32x4*>(dst) = v;
             }
     };
+    // piece i of this lane's granule lies past k in the last round (TAIL)
+    auto w_past = [&](int i) { return b * kGranule + i * (16 / S) >= tail; };
     // this lane's weight granules of round g (columns past n read column n-1)
     // With W32 (an expert's matrix spans under 4 GB) a load's address is a
     // block-uniform base (expert and round, in scalar registers) plus a
     // 32-bit lane offset fixed for the job, so the steady loop spends no
     // vector instructions on 64-bit addresses.
-    // piece i of this lane lies past k in the last round (TAIL)
-    auto w_past = [&](int i) { return b * kGranule + i * (16 / S) >= tail; };
     auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
         const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)j.wexp * a.stride;
 #pragma unroll
