@@ -59,6 +59,11 @@ int matmul_id_shared_map(const eidm_shape* shape, int route, const void* weights
 hipError_t launch_direct(const MatmulArgs& a, hipStream_t stream);
 hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                           hipStream_t stream);
+// The Grouped kernel on the 16x16x1 matrix-core step (16-bit weights, vector
+// rows, at least two rounds, 32-bit offsets); launch_grouped picks it when
+// grouped16_supported says so.
+bool grouped16_supported(const MatmulArgs& a);
+hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,
                           const float* gates, float* out, hipStream_t stream);
 bool moe_direct_supported(uint32_t top_k, uint32_t n_experts);

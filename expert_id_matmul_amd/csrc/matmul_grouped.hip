@@ -934,6 +934,7 @@ hipError_t launch_dt(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
 
 hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                           hipStream_t stream) {
+    if (grouped16_supported(a)) return launch_grouped16(a, buf, device_cus, stream);
     switch (a.dtype) {
     case kDtypeF32: return launch_dt<kDtypeF32>(a, buf, device_cus, stream);
     case kDtypeF16: return launch_dt<kDtypeF16>(a, buf, device_cus, stream);
