@@ -7,17 +7,21 @@ gate-weighted combine, all in the library's HIP kernels.
 Headline (`value`): decode, m=1, k=4096, n=1536, top-8 of 256 bf16 experts,
 as effective GB/s of touched expert weights (8 x 1536 x 4096 x 2 B per step)
 over the whole step.  Decode is timed cold: step i routes with the experts
-relabelled so that its picks are experts 8i..8i+7, so 32 consecutive steps
-sweep all 3.2 GB of weights and none is served from the 256 MB Infinity
-Cache.  The prefill configurations (m=2048 down projection with per-slot
-input; m=512 balanced and maximally skewed) are reported next to it in
-TFLOP/s.
+relabelled so that its picks are experts 8(i mod 32)..8(i mod 32)+7, so 32
+consecutive steps sweep all 3.2 GB of weights and none is served from the
+256 MB Infinity Cache.  The prefill configurations (m=2048 down projection
+with per-slot input; m=512 balanced and maximally skewed) are reported next
+to it in TFLOP/s.
 
 A decode step is one launch of the fused kernel (route, Direct matmul and
-combine); 32 steps are captured into a HIP graph and replayed, and HIP
-events on the replaying stream bracket the timed replays, so the per-step
-time is that kernel's average launch duration.  The prefill matmul calls
-are timed one by one with HIP events on the stream the kernels run on.
+combine).  Exactly --steps steps are captured into one HIP graph and replayed
+once between two HIP events on the replaying stream, so the per-step time is
+that kernel's average launch duration.  The GPU clocks take a few hundred
+milliseconds of load to ramp up, so every measurement is preceded by at
+least --warmup steps and at least half a second of the same work; the line
+reports both what was asked and what ran.  Prefill matmul calls (id map +
+Grouped kernel) are timed the same way, after their own warm-up: a graph of
+back-to-back calls between HIP events.
 """
 from __future__ import annotations
 
@@ -42,6 +46,7 @@ from expert_id_matmul_amd import workloads as W  # noqa: E402
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 F32_PEAK = 157.3e12          # flop/s, MI355X dense f32 matrix
 ROT = 32                     # decode steps per full sweep of the experts
+PREFILL_STEPS = 16           # matmul calls per timed prefill graph
 
 
 def _dev(a: np.ndarray) -> torch.Tensor:
@@ -66,45 +71,70 @@ def _relabel(n_experts: int, picks: np.ndarray, target: np.ndarray) -> np.ndarra
     return p
 
 
+WARMUP_FLOOR_S = 0.5  # seconds of the same work before any timed region
+SPIN_CYCLES = 200_000  # ~80 us of GPU spin: the host enqueues the timed work meanwhile
+
+
+def _capture(step_fn, n: int, start: int = 0) -> torch.cuda.CUDAGraph:
+    """A HIP graph of step_fn(start) .. step_fn(start + n - 1), captured on a
+    side stream after one eager pass of the same steps."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(start, start + n):
+            step_fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(start, start + n):
+            step_fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
 class Timed:
-    """Capture `steps` calls of step_fn into a graph, replay it, and time it."""
+    """Warm up on a graph of `warm_n` steps for at least `warmup` steps and
+    WARMUP_FLOOR_S seconds, then time one graph of exactly `steps` steps."""
 
-    def __init__(self, step_fn, steps_per_graph: int):
+    def __init__(self, step_fn, warm_n: int):
         self.step_fn = step_fn
-        self.n = steps_per_graph
-        self.graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            for i in range(self.n):  # eager warm-up on the capture stream
-                step_fn(i)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(self.graph):
-            for i in range(self.n):
-                step_fn(i)
-        torch.cuda.synchronize()
+        self.warm = _capture(step_fn, warm_n)
+        self.warm_n = warm_n
 
-    def run(self, steps: int, warmup: int):
-        reps = max(1, -(-steps // self.n))
-        wreps = max(1, -(-warmup // self.n)) if warmup > 0 else 0
-        for _ in range(wreps):
-            self.graph.replay()
+    def warm_up(self, warmup: int, floor_s: float = WARMUP_FLOOR_S):
+        done, t0 = 0, time.perf_counter()
+        while done < warmup or time.perf_counter() - t0 < floor_s:
+            self.warm.replay()
+            done += self.warm_n
+            if done % (self.warm_n * 16) == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(reps):
-            self.graph.replay()
-        end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        done = reps * self.n
-        return {"steps": done, "gpu_ms_per_step": start.elapsed_time(end) / done,
-                "wall_ms_per_step": wall * 1e3 / done}
+        return done, time.perf_counter() - t0
+
+    def run(self, steps: int, warmup: int, repeats: int = 1):
+        timed = _capture(self.step_fn, steps)
+        wsteps, wsecs = self.warm_up(warmup)
+        times = []
+        for _ in range(repeats):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # a short GPU spin ahead of the start event keeps the GPU busy
+            # while the host submits the graph, so the interval holds the
+            # steps only
+            torch.cuda._sleep(SPIN_CYCLES)
+            start.record()
+            timed.replay()
+            end.record()
+            torch.cuda.synchronize()
+            times.append((start.elapsed_time(end), time.perf_counter() - t0))
+        gpu_ms, wall_s = times[0]
+        return {"steps": steps, "gpu_ms_per_step": gpu_ms / steps, "wall_ms_per_step": wall_s * 1e3 / steps,
+                "warmup_steps_run": wsteps, "warmup_s": round(wsecs, 3),
+                "repeats_gpu_ms_per_step": [t[0] / steps for t in times]}
 
 
-SPIN_CYCLES = 200_000  # ~80 us of GPU spin: the host enqueues the timed launch meanwhile
 
 
 def kernel_times(call, steps: int, before=None, after=None):
@@ -178,15 +208,16 @@ def bench_decode(lib, steps: int, warmup: int):
     res = timed.run(steps, warmup)
     # the graph's last step against the same step run eagerly, and against
     # the three separate calls
+    last = steps - 1
     graph_out, graph_ids = out.clone(), ids.clone()
-    step(ROT - 1)
+    step(last)
     torch.cuda.synchronize()
     assert torch.equal(graph_out, out) and torch.equal(graph_ids, ids), "graph replay differs from eager"
-    assert sorted(graph_ids.cpu().numpy()[0].tolist()) == list(range(8 * (ROT - 1), 8 * ROT))
-    step_unfused(ROT - 1)
+    assert sorted(graph_ids.cpu().numpy()[0].tolist()) == list(range(8 * (last % ROT), 8 * (last % ROT) + 8))
+    step_unfused(last)
     torch.cuda.synchronize()
     assert torch.equal(graph_out.view(torch.int32), out.view(torch.int32)), "fused and unfused steps differ"
-    unfused = Timed(step_unfused, ROT).run(max(ROT, steps // 4), max(ROT, warmup // 4))
+    unfused = Timed(step_unfused, ROT).run(ROT * 4, ROT, repeats=1)
     nbytes = decode_bytes(wl)
     t = res["gpu_ms_per_step"] * 1e-3
     res.update({
@@ -231,17 +262,17 @@ def bench_prefill(lib, name: str, steps: int, warmup: int):
         matmul(i)
         lib.combine(y, gates, out)
 
-    timed = Timed(step, 4)
-    # prefill steps are ~40x longer than decode steps: fewer of them
-    res = timed.run(max(16, steps // 16), max(8, warmup // 64) if warmup else 0)
-    mm = kernel_times(matmul, max(16, steps // 32))
+    # whole steps (route, matmul, combine), then the matmul call alone
+    res = Timed(step, 4).run(PREFILL_STEPS, 8)
+    mm = Timed(matmul, 4).run(PREFILL_STEPS, 8, repeats=3)
     flops = 2.0 * wl.routed_rows * wl.n * wl.k
-    avg = float(np.mean(mm))
+    per_call = float(np.median(mm["repeats_gpu_ms_per_step"]))
     res.update({
         "flops": flops,
         "tflops": flops / (res["gpu_ms_per_step"] * 1e-3) / 1e12,
-        "grouped_ms": {"avg": avg, **_percentiles(mm), "n": len(mm)},
-        "grouped_tflops": flops / (avg * 1e-3) / 1e12,
+        "matmul_ms": {"per_call": per_call, "repeats": mm["repeats_gpu_ms_per_step"],
+                      "calls_per_repeat": PREFILL_STEPS, "warmup_s": mm["warmup_s"]},
+        "grouped_tflops": flops / (per_call * 1e-3) / 1e12,
     })
     # Direct on the same inputs, for the route comparison (not the headline)
     dm = kernel_times(lambda i: matmul(i, B.DIRECT), 3)
@@ -273,7 +304,7 @@ def bench_ffn(lib, steps: int, warmup: int):
         lib.moe_ffn(shape, B.AUTO, wdev["gate"], wdev["up"], wdev["down"], x, logits, bias, ids, gates, out,
                     scratch)
 
-    res = Timed(step, 4).run(max(16, steps // 16), max(8, warmup // 64) if warmup else 0)
+    res = Timed(step, 4).run(PREFILL_STEPS, 8)
     flops = 3 * 2.0 * fw.m * fw.top_k * fw.hidden * fw.inter
     res["flops"] = flops
     res["tflops"] = flops / (res["gpu_ms_per_step"] * 1e-3) / 1e12
@@ -317,47 +348,100 @@ def decode_traffic():
 
 
 # ---------------------------------------------------------------------- CPU oracle
-def cpu_baseline(budget_s: float = 15.0):
-    """The CPU oracle, as it stands, on a bounded sample of the decode workload:
-    whole decode steps (route, the 8 routed rows' matmul, combine) repeated
-    until the budget is spent; one host thread."""
+def _host_cpus() -> dict:
+    """Host core count (affinity and online) and the CPU model name."""
+    model = platform.processor() or platform.machine()
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ln.lower().startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"usable": usable, "online": os.cpu_count() or usable, "model": model}
+
+
+def _median_time(fn, runs: int = 3) -> float:
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline():
+    """The CPU oracle, as it stands (double-precision sums, one routine per
+    output), on bounded samples of two workloads, each the median of 3 runs,
+    on one host thread and on every usable host thread (the outputs split into
+    contiguous ranges):
+      decode: whole steps (route + the 8 routed rows x 1536 x 4096 bf16 matmul
+              + combine), 4 steps per run, in GB/s of touched weights;
+      prefill balanced: the 256 routed rows of experts 0-7 (m=512, k=2048,
+              n=768, top-8 of 128 bf16), in GFLOP/s.
+    `value` is the all-threads decode figure."""
     import oracle
 
+    host = _host_cpus()
+    threads = host["usable"]
+    legs = {}
+    # decode
     wl = W.WORKLOADS["decode"]
-    logits = W.router_logits(wl)
-    bias = W.router_bias(wl)
-    x = W.activations(wl)
-    ids, _, _, _ = oracle.route(logits, bias, wl.top_k)
+    logits, bias, x = W.router_logits(wl), W.router_bias(wl), W.activations(wl)
+    ids0, _, _, _ = oracle.route(logits, bias, wl.top_k)
     # the touched experts packed at indices 0..7 (placement does not change y)
     packed = np.concatenate([W.expert_weights(wl, int(e)).contiguous().view(torch.uint8).numpy().reshape(-1)
-                             for e in ids[0]])
+                             for e in ids0[0]])
     local_ids = np.arange(wl.top_k, dtype=np.uint32)[None]
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        ids_s, gates_s, _, _ = oracle.route(logits, bias, wl.top_k)
-        y = oracle.matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.top_k, wl.stride, wl.layout,
-                             packed, x, local_ids)
-        oracle.combine(y, gates_s, wl.top_k)
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = (time.perf_counter() - t0) / n
     touched = wl.top_k * wl.n * wl.k * W.DTYPE_SIZE[wl.dtype]
-    return {"value": touched / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} whole decode steps (route + 8x1536x4096 bf16 matmul + combine), "
-                      f"{dt * 1e3:.0f} ms each, 1 thread, {platform.processor() or platform.machine()}"}
+    steps = 4
+    for th in (1, threads):
+        def run(th=th):
+            for _ in range(steps):
+                _, g, _, _ = oracle.route(logits, bias, wl.top_k)
+                y = oracle.matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.top_k, wl.stride, wl.layout,
+                                             packed, x, local_ids, th)
+                oracle.combine(y, g, wl.top_k)
+        t = _median_time(run) / steps
+        legs[f"decode_{th}t"] = {"value": touched / t / 1e9, "unit": "GB/s", "threads": th,
+                                 "ms_per_step": t * 1e3}
+    # prefill balanced sample: routed rows of experts 0..7, as a slotted problem
+    wl = W.WORKLOADS["prefill_balanced"]
+    n_e = 8
+    packed = np.concatenate([W.expert_weights(wl, e).contiguous().view(torch.uint8).numpy().reshape(-1)
+                             for e in range(n_e)])
+    ids = W.ids(wl).reshape(-1)
+    rows = np.nonzero(ids < n_e)[0]
+    xs = W.activations(wl)[rows // wl.top_k]
+    sids = ids[rows].astype(np.uint32)[:, None]
+    flops = 2.0 * rows.size * wl.n * wl.k
+    for th in (1, threads):
+        t = _median_time(lambda th=th: oracle.matmul_id_threads(wl.dtype, rows.size, wl.n, wl.k, 1, n_e, wl.stride,
+                                                                 W.LAYOUT_SLOTTED, packed, xs, sids, th))
+        legs[f"prefill_balanced_{th}t"] = {"value": flops / t / 1e9, "unit": "GFLOP/s", "threads": th,
+                                           "s_per_run": t}
+    best = legs[f"decode_{threads}t"]
+    return {"value": best["value"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"decode: {steps} whole steps per run (route + 8x1536x4096 bf16 matmul + combine); "
+                      f"prefill balanced: the {rows.size} routed rows of experts 0-{n_e - 1} "
+                      f"({flops / 1e9:.2f} GFLOP); median of 3 runs each, on 1 and {threads} threads",
+            "host_cpus": host, "legs": legs}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the clocks take a few hundred milliseconds of load to ramp up: the
-    # default warm-up is about half a second of decode steps
-    ap.add_argument("--steps", type=int, default=4096)
-    ap.add_argument("--warmup", type=int, default=16384)
+    ap.add_argument("--steps", type=int, default=640, help="decode steps timed (exactly this many)")
+    ap.add_argument("--warmup", type=int, default=64,
+                    help="decode warm-up steps (at least; the warm-up also lasts at least half a second)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ffn", action="store_true", help="skip the expert-FFN line")
     ap.add_argument("--no-decode", action="store_true",
                     help="prefill configurations only (the line then has no headline value)")
     ap.add_argument("--prefill", default="down_proj,prefill_balanced,prefill_skewed",
@@ -369,6 +453,9 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the expert-ID matmul path here has no multi-GPU "
               "form (expert or column sharding is a design, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -383,26 +470,29 @@ def main():
     lib = B.load()
     dec = None
     if not args.no_decode:
-        print(f"[bench] decode: {args.steps} steps, warmup {args.warmup}", file=sys.stderr, flush=True)
+        print(f"[bench] decode: {args.steps} steps, warmup {args.warmup} (and >= {WARMUP_FLOOR_S} s)",
+              file=sys.stderr, flush=True)
         dec = bench_decode(lib, args.steps, args.warmup)
+        print(f"[bench] decode warm-up ran {dec['warmup_steps_run']} steps in {dec['warmup_s']} s",
+              file=sys.stderr, flush=True)
     prefill = {}
     if not args.no_prefill:
         for name in [p for p in args.prefill.split(",") if p]:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             prefill[name] = bench_prefill(lib, name, args.steps, args.warmup)
     ffn = None
-    if not args.no_prefill:
+    if not args.no_prefill and not args.no_ffn:
         print("[bench] ffn_prefill", file=sys.stderr, flush=True)
         ffn = bench_ffn(lib, args.steps, args.warmup)
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not args.no_decode:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline()
     prefill_out = {k: {"tflops_step": round(v["tflops"], 2),
                        "tflops_matmul": round(v["grouped_tflops"], 2),
                        "frac_f32_peak_matmul": round(v["grouped_tflops"] * 1e12 / F32_PEAK, 4),
                        "ms_per_step": round(v["gpu_ms_per_step"], 4),
-                       "matmul_ms": v["grouped_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
+                       "matmul_ms": v["matmul_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
                    for k, v in prefill.items()}
     if dec is None:
         print(json.dumps({"prefill": prefill_out}), flush=True)
@@ -414,6 +504,8 @@ def main():
         "n_gpus": 1,
         "steps": dec["steps"],
         "warmup": args.warmup,
+        "warmup_steps_run": dec["warmup_steps_run"],
+        "warmup_s": dec["warmup_s"],
         "ms_per_step": round(dec["gpu_ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -274,15 +274,22 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
     };
 
     f32x16 acc[2][4];
-    // slice sums in the canonical pairing, and the stores
+    // slice sums in the canonical pairing, and the stores.  The eight output
+    // rows' offsets are read from LDS first, so their latency is paid once;
+    // each total is formed outside the store's branch.
     auto finish = [&](const G16Job& j) {
         const int col = (int)j.col0 + wave * kG16WN + l16;
         const bool nan_rows = j.e == a.n_experts;
+        const bool col_ok = col < n;
+        uint32_t yo[2][4];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) yo[rt][v] = yoff_s[j.slot + 16 * rt + 4 * blk + v];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = 16 * rt + 4 * blk + v;
                 float u[4];
 #pragma unroll
                 for (int bb = 0; bb < 4; ++bb) {
@@ -293,16 +300,14 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
                 }
                 // (s, s^2) pairs blocks 0-2 and 1-3, then (s, s^1)
                 const float total = (u[0] + u[2]) + (u[1] + u[3]);
-                if (row < (int)j.rc && col < n) {
-                    const uint32_t yo = yoff_s[j.slot + row] + (uint32_t)col;
-                    a.output[(size_t)yo] = nan_rows ? quiet_nan() : total;
-                }
+                if (col_ok && 16 * rt + 4 * blk + v < (int)j.rc)
+                    a.output[(size_t)(yo[rt][v] + (uint32_t)col)] = nan_rows ? quiet_nan() : total;
             }
     };
 
     // ---- prologue: weights of rounds 0 and 1, activations of rounds 0, 1
     // and 2 of job 0 (the last stay staged in registers)
-    LoadState Lc = load_state(decode(0));
+    LoadState Lc = load_state(decode(0));  // decode(0) also fills the first chunk
     g16u32x4 ring[2][4];
     f32x4 stg[kG16Stage];
     {

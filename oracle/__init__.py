@@ -26,7 +26,7 @@ def build() -> str:
     """Compile the oracle (no fast-math, no contraction: every operation is
     the one written)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Werror", _SRC, "-o", _LIB + ".tmp", "-lm"]
+           "-Wall", "-Werror", "-pthread", _SRC, "-o", _LIB + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(_LIB + ".tmp", _LIB)
     return _LIB
@@ -49,6 +49,8 @@ def _load():
     lib.oracle_route.argtypes = [P, P, u32, u32, u32, i32, P, P, P, P]
     lib.oracle_matmul_id.restype = i32
     lib.oracle_matmul_id.argtypes = [i32, u32, u32, u32, u32, u32, u64, i32, P, P, P, P]
+    lib.oracle_matmul_id_threads.restype = i32
+    lib.oracle_matmul_id_threads.argtypes = [i32, u32, u32, u32, u32, u32, u64, i32, P, P, P, P, i32]
     lib.oracle_matmul_id_at.restype = i32
     lib.oracle_matmul_id_at.argtypes = [i32, u32, u32, u32, u32, u32, u64, i32, P, P, P, u64, P, P, P]
     lib.oracle_combine.restype = i32
@@ -120,6 +122,24 @@ def matmul_id(dtype: int, m: int, n: int, k: int, top_k: int, n_experts: int, st
                                   _ptr(w), _ptr(x), _ptr(ids), _ptr(y))
     if rc != 0:
         raise ValueError(f"oracle_matmul_id failed ({rc})")
+    return y
+
+
+def matmul_id_threads(dtype: int, m: int, n: int, k: int, top_k: int, n_experts: int, stride: int,
+                      layout: int, weights: np.ndarray, x: np.ndarray, ids: np.ndarray,
+                      threads: int) -> np.ndarray:
+    """matmul_id split over `threads` host threads (the same values)."""
+    w = _c(weights, np.uint8).reshape(-1)
+    assert w.size >= required_weight_bytes(dtype, n, k, n_experts, stride)
+    x = _c(x, np.float32)
+    ids = _c(ids, np.uint32)
+    rows_in = m * top_k if layout == SLOTTED else m
+    assert x.size == rows_in * k and ids.size == m * top_k
+    y = np.empty((m * top_k, n), dtype=np.float64)
+    rc = _load().oracle_matmul_id_threads(dtype, m, n, k, top_k, n_experts, stride, layout,
+                                          _ptr(w), _ptr(x), _ptr(ids), _ptr(y), int(threads))
+    if rc != 0:
+        raise ValueError(f"oracle_matmul_id_threads failed ({rc})")
     return y
 
 

@@ -18,6 +18,7 @@
  * example); the pin of each is named in its comment.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -210,6 +211,78 @@ int oracle_matmul_id(int dtype, uint32_t m, uint32_t n, uint32_t k, uint32_t top
             y[r * n + j] = one_output(dtype, n, k, top_k, n_experts, stride, layout,
                                       (const uint8_t*)weights, x, ids, r, j);
     return 0;
+}
+
+/*
+ * oracle_matmul_id on `threads` host threads: the outputs (routed row,
+ * column), numbered r*n + j, are split into `threads` contiguous ranges and
+ * each thread evaluates its range with the same per-output routine.  The
+ * values are those of oracle_matmul_id bit for bit (each output is computed
+ * the same way, by one thread).  Used for the host-core baseline and for
+ * full-size checks; pin: equality with oracle_matmul_id.
+ */
+typedef struct {
+    int dtype;
+    uint32_t n, k, top_k, n_experts;
+    uint64_t stride;
+    int layout;
+    const uint8_t* w;
+    const float* x;
+    const uint32_t* ids;
+    double* y;
+    uint64_t begin, end;
+} mm_part;
+
+static void* mm_worker(void* arg) {
+    const mm_part* p = (const mm_part*)arg;
+    for (uint64_t o = p->begin; o < p->end; ++o) {
+        const uint64_t r = o / p->n;
+        const uint32_t j = (uint32_t)(o % p->n);
+        p->y[o] = one_output(p->dtype, p->n, p->k, p->top_k, p->n_experts, p->stride, p->layout, p->w, p->x,
+                             p->ids, r, j);
+    }
+    return NULL;
+}
+
+int oracle_matmul_id_threads(int dtype, uint32_t m, uint32_t n, uint32_t k, uint32_t top_k,
+                             uint32_t n_experts, uint64_t stride, int layout, const void* weights,
+                             const float* x, const uint32_t* ids, double* y, int threads) {
+    if (!dtype_size(dtype) || m == 0 || n == 0 || k == 0 || top_k == 0 || n_experts == 0) return -1;
+    if (threads < 1 || threads > 1024) return -1;
+    const uint64_t total = (uint64_t)m * top_k * n;
+    mm_part* parts = (mm_part*)calloc((size_t)threads, sizeof(mm_part));
+    pthread_t* tids = (pthread_t*)calloc((size_t)threads, sizeof(pthread_t));
+    if (!parts || !tids) {
+        free(parts);
+        free(tids);
+        return -2;
+    }
+    int started = 0, rc = 0;
+    for (int t = 0; t < threads; ++t) {
+        mm_part* p = &parts[t];
+        p->dtype = dtype;
+        p->n = n;
+        p->k = k;
+        p->top_k = top_k;
+        p->n_experts = n_experts;
+        p->stride = stride;
+        p->layout = layout;
+        p->w = (const uint8_t*)weights;
+        p->x = x;
+        p->ids = ids;
+        p->y = y;
+        p->begin = total * (uint64_t)t / (uint64_t)threads;
+        p->end = total * (uint64_t)(t + 1) / (uint64_t)threads;
+        if (pthread_create(&tids[t], NULL, mm_worker, p) != 0) {
+            rc = -3;
+            break;
+        }
+        ++started;
+    }
+    for (int t = 0; t < started; ++t) pthread_join(tids[t], NULL);
+    free(parts);
+    free(tids);
+    return rc;
 }
 
 /*

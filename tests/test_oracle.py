@@ -203,6 +203,20 @@ def test_spot_outputs_equal_full_outputs():
     assert np.array_equal(got, y[rows, cols])
 
 
+@pytest.mark.parametrize("threads", [1, 2, 7, 64])
+def test_threaded_outputs_equal_full_outputs(threads):
+    """The host-thread split of the oracle (used for the CPU baseline and the
+    full-size checks) computes every output with the same routine."""
+    wl = TAIL_SHAPES[3]
+    wb = padded_weights(wl)
+    x = W.activations(wl)
+    ids = W.ids(wl)
+    y = run_oracle(wl, wb, x, ids)
+    got = oracle.matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride,
+                                   wl.layout, wb, x, ids, threads)
+    assert np.array_equal(got.view(np.uint64), y.view(np.uint64))
+
+
 def test_out_of_range_id_gives_nan_row_only():
     wl = W.WORKLOADS["tiny"]
     wb = padded_weights(wl)
