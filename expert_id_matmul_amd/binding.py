@@ -25,7 +25,7 @@ EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk
            "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward",
            "eidm_validate_ids", "eidm_plan_create", "eidm_plan_destroy", "eidm_plan_freeze",
            "eidm_plan_route", "eidm_calibration_workspace_bytes", "eidm_calibrate",
-           "eidm_matmul_id_planned", "eidm_moe_ffn_scratch_bytes", "eidm_moe_ffn"]
+           "eidm_matmul_id_planned", "eidm_moe_ffn_scratch_bytes", "eidm_moe_ffn", "eidm_matmul_id_noalloc"]
 
 
 class Shape(ctypes.Structure):
@@ -159,6 +159,9 @@ class Library:
         L.eidm_matmul_id.restype = i32
         L.eidm_matmul_id.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, P, u64, P,
                                      ctypes.POINTER(ctypes.c_int)]
+        L.eidm_matmul_id_noalloc.restype = i32
+        L.eidm_matmul_id_noalloc.argtypes = [ctypes.POINTER(Shape), i32, P, u64, P, P, P, P,
+                                             ctypes.POINTER(ctypes.c_int)]
         L.eidm_combine.restype = i32
         L.eidm_combine.argtypes = [u32, u32, u32, P, P, P, P]
         L.eidm_validate_ids.restype = i32
@@ -250,6 +253,18 @@ class Library:
         self._check(self.lib.eidm_matmul_id(ctypes.byref(shape), route, _ptr(weights), weight_bytes,
                                             _ptr(input), _ptr(ids), _ptr(output), _ptr(scratch),
                                             sbytes, _stream(stream), ctypes.byref(taken)))
+        return taken.value
+
+    def matmul_id_noalloc(self, shape: Shape, route: int, weights, input, ids, output,
+                          weight_bytes: int | None = None, stream=None) -> int:
+        """eidm_matmul_id with the library's static map array (no scratch)."""
+        if weight_bytes is None:
+            weight_bytes = _nbytes(weights)
+        self._check_matmul_buffers(shape, DIRECT, weights, weight_bytes, input, ids, output, None)
+        taken = ctypes.c_int(-1)
+        self._check(self.lib.eidm_matmul_id_noalloc(ctypes.byref(shape), route, _ptr(weights), weight_bytes,
+                                                    _ptr(input), _ptr(ids), _ptr(output), _stream(stream),
+                                                    ctypes.byref(taken)))
         return taken.value
 
     def combine(self, y, gates, out, stream=None) -> None:

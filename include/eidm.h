@@ -211,6 +211,23 @@ int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint
                    uint64_t scratch_bytes, void* stream, int* route_taken);
 
 /*
+ * eidm_matmul_id for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and bits, with no scratch argument.  The Grouped
+ * route's id -> row map lives in a device array the library owns, 8 MiB per
+ * GPU, held from the first call on that GPU until the process ends; the call
+ * itself allocates nothing.  Arguments as in eidm_matmul_id (weights, input,
+ * ids and output are still the caller's).  GROUPED fails with EIDM_E_SIZE,
+ * before anything is enqueued, when the map needs more than 8 MiB
+ * (eidm_query's scratch_bytes); AUTO then runs Direct.  Every call on one
+ * GPU uses the same array, so calls whose work overlaps in time on one GPU
+ * (several streams or host threads) race; issue them on one stream.
+ */
+int eidm_matmul_id_noalloc(const eidm_shape* shape, int route, const void* weights, uint64_t weight_bytes,
+                           const float* input, const uint32_t* ids, float* output, void* stream,
+                           int* route_taken);
+
+/*
  * Gate-weighted sum over slots (cortiq-engine mimo_moe.rs Dynamic::run;
  * hf2q dense_ffn_arena.rs MoeFfnArena's weighted reduce):
  *   out[t, j] = sum_s gates[t, s] * y[t*top_k + s, j]

@@ -124,6 +124,22 @@ def test_matmul_rejects_before_launch(lib):
     assert _matmul(lib, sb, weights=FAKE + 3, wbytes=10 ** 6)[0] == B.E_ALIGN
 
 
+def test_noalloc_rejects_a_map_beyond_its_static_array_before_launch(lib):
+    # 400000 tokens x top-8: the id -> row map alone needs about 12.8 MB, above
+    # the 8 MiB array; the call fails on the host (no pointer is touched)
+    s = B.make_shape(B.BF16, 400000, 64, 256, 8, 16, 64 * 256 * 2)
+    assert lib.query(s, B.GROUPED).scratch_bytes > 8 << 20
+    taken = ctypes.c_int(-1)
+    rc = lib.lib.eidm_matmul_id_noalloc(ctypes.byref(s), B.GROUPED, None, 0, None, None, None, None,
+                                        ctypes.byref(taken))
+    assert rc == B.E_SIZE and "static array" in lib.last_error()
+    assert taken.value == -1
+    # a bad shape is rejected the same way as by eidm_matmul_id
+    bad = B.make_shape(B.BF16, 0, 64, 256, 8, 16, 64 * 256 * 2)
+    assert lib.lib.eidm_matmul_id_noalloc(ctypes.byref(bad), B.AUTO, None, 0, None, None, None, None,
+                                          None) == B.E_INVALID
+
+
 def test_route_map_combine_reject_bad_arguments(lib):
     L = lib.lib
     P = ctypes.c_void_p
