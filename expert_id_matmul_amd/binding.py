@@ -25,7 +25,14 @@ EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk
            "eidm_map_scratch_bytes", "eidm_matmul_id", "eidm_combine", "eidm_moe_forward",
            "eidm_validate_ids", "eidm_plan_create", "eidm_plan_destroy", "eidm_plan_freeze",
            "eidm_plan_route", "eidm_calibration_workspace_bytes", "eidm_calibrate",
-           "eidm_matmul_id_planned", "eidm_moe_ffn_scratch_bytes", "eidm_moe_ffn", "eidm_matmul_id_noalloc"]
+           "eidm_matmul_id_planned", "eidm_moe_ffn_scratch_bytes", "eidm_moe_ffn", "eidm_matmul_id_noalloc",
+           "eidm_last_dispatch", "eidm_plan_set_limits"]
+
+# eidm_kernel (include/eidm.h): kernels a call can launch
+KERNELS = {1: "route", 2: "map_one_pass", 3: "map_histogram", 4: "map_scatter", 5: "direct",
+           6: "grouped_16x16", 7: "grouped_stream", 8: "grouped_job", 9: "combine",
+           10: "fused_decode", 11: "silu_mul", 12: "validate", 13: "proof"}
+MAX_RECORDED_LAUNCHES = 16
 
 
 class Shape(ctypes.Structure):
@@ -68,7 +75,7 @@ class Calibration(ctypes.Structure):
     """eidm_calibration (include/eidm.h)."""
     _fields_ = [("struct_size", ctypes.c_uint32), ("route", ctypes.c_int32),
                 ("grouped_legal", ctypes.c_int32), ("bit_identical", ctypes.c_int32),
-                ("reason", ctypes.c_int32), ("reserved0", ctypes.c_int32)] + [
+                ("reason", ctypes.c_int32), ("submissions", ctypes.c_uint32)] + [
         (name, ctypes.c_double * 2) for name in (
             "direct_wall_p25", "direct_wall_median", "direct_wall_p75", "direct_gpu_median",
             "grouped_wall_p25", "grouped_wall_median", "grouped_wall_p75", "grouped_gpu_median")]
@@ -79,7 +86,32 @@ class Calibration(ctypes.Structure):
 
 
 CAL_REASONS = ["grouped wins", "grouped not legal", "grouped failed", "not bit identical",
-               "wall median", "wall quartiles", "gpu median"]
+               "wall median", "wall quartiles", "gpu median", "budget"]
+CAL_BUDGET = 7
+GATE_SUBMISSIONS = 27  # host waits of one complete calibration gate
+
+
+class CalibrationLimits(ctypes.Structure):
+    """eidm_calibration_limits (include/eidm.h)."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("max_cases", ctypes.c_uint32),
+                ("max_submissions", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+                ("max_elapsed_ms", ctypes.c_uint64)]
+
+
+class Launch(ctypes.Structure):
+    """eidm_launch (include/eidm.h)."""
+    _fields_ = [("kernel", ctypes.c_int32), ("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
+                ("lds_bytes", ctypes.c_uint32)]
+
+
+class Dispatch(ctypes.Structure):
+    """eidm_dispatch (include/eidm.h)."""
+    _fields_ = [("struct_size", ctypes.c_uint32), ("route", ctypes.c_int32),
+                ("dispatch_count", ctypes.c_uint32), ("recorded", ctypes.c_uint32),
+                ("launches", Launch * MAX_RECORDED_LAUNCHES)]
+
+    def kernels(self) -> list[str]:
+        return [KERNELS.get(self.launches[i].kernel, "?") for i in range(self.recorded)]
 
 
 class EidmError(RuntimeError):
@@ -171,7 +203,11 @@ class Library:
         L.eidm_plan_destroy.restype = None
         L.eidm_plan_destroy.argtypes = [P]
         L.eidm_plan_freeze.restype = i32
-        L.eidm_plan_freeze.argtypes = [P]
+        L.eidm_plan_freeze.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+        L.eidm_plan_set_limits.restype = i32
+        L.eidm_plan_set_limits.argtypes = [P, ctypes.POINTER(CalibrationLimits)]
+        L.eidm_last_dispatch.restype = i32
+        L.eidm_last_dispatch.argtypes = [ctypes.POINTER(Dispatch)]
         L.eidm_plan_route.restype = i32
         L.eidm_plan_route.argtypes = [P, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int)]
         L.eidm_calibration_workspace_bytes.restype = u64
@@ -200,6 +236,13 @@ class Library:
 
     def abi_version(self) -> int:
         return self.lib.eidm_abi_version()
+
+    def last_dispatch(self) -> Dispatch:
+        """The dispatch receipt of this thread's last library call."""
+        d = Dispatch()
+        d.struct_size = ctypes.sizeof(Dispatch)
+        self._check(self.lib.eidm_last_dispatch(ctypes.byref(d)))
+        return d
 
     def _check_matmul_buffers(self, shape, route, weights, weight_bytes, input, ids, output,
                               scratch) -> None:
@@ -362,8 +405,17 @@ class Plan:
                                                     _nbytes(workspace), _stream(stream), ctypes.byref(rec)))
         return rec
 
-    def freeze(self) -> None:
-        self.lib._check(self.lib.lib.eidm_plan_freeze(ctypes.c_void_p(self.handle)))
+    def set_limits(self, max_elapsed_ms: int = 15000, max_cases: int = 256,
+                   max_submissions: int = 6145) -> None:
+        lim = CalibrationLimits(ctypes.sizeof(CalibrationLimits), max_cases, max_submissions, 0,
+                                max_elapsed_ms)
+        self.lib._check(self.lib.lib.eidm_plan_set_limits(ctypes.c_void_p(self.handle), ctypes.byref(lim)))
+
+    def freeze(self) -> int:
+        """Freeze the plan; returns how many Grouped entries the deadline turned into Direct."""
+        n = ctypes.c_uint32(0)
+        self.lib._check(self.lib.lib.eidm_plan_freeze(ctypes.c_void_p(self.handle), ctypes.byref(n)))
+        return n.value
 
     def route(self, shape: Shape) -> int:
         r = ctypes.c_int(-1)

@@ -63,7 +63,7 @@ hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, m, top_k, n,
                        y, gates, out, vec);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_COMBINE, (uint32_t)blocks, 256, 0);
 }
 
 }  // namespace eidm

@@ -21,9 +21,39 @@
 
 namespace {
 thread_local std::string g_error;
+thread_local eidm_dispatch g_receipt;
+thread_local int g_receipt_depth = 0;
 }  // namespace
 
 namespace eidm {
+
+ReceiptScope::ReceiptScope() {
+    if (g_receipt_depth++ == 0) {
+        g_receipt = eidm_dispatch{};
+        g_receipt.struct_size = sizeof(eidm_dispatch);
+    }
+}
+
+ReceiptScope::~ReceiptScope() { --g_receipt_depth; }
+
+void receipt_route(int route) { g_receipt.route = route; }
+
+void note_launch(int kernel, uint32_t grid, uint32_t block, uint32_t lds_bytes) {
+    if (g_receipt.recorded < EIDM_MAX_RECORDED_LAUNCHES) {
+        eidm_launch& l = g_receipt.launches[g_receipt.recorded++];
+        l.kernel = kernel;
+        l.grid = grid;
+        l.block = block;
+        l.lds_bytes = lds_bytes;
+    }
+    ++g_receipt.dispatch_count;
+}
+
+hipError_t launched(int kernel, uint32_t grid, uint32_t block, uint32_t lds_bytes) {
+    const hipError_t err = hipGetLastError();
+    if (err == hipSuccess) note_launch(kernel, grid, block, lds_bytes);
+    return err;
+}
 
 int api_fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -282,6 +312,16 @@ int eidm_abi_version(void) { return EIDM_ABI_VERSION; }
 
 const char* eidm_last_error(void) { return g_error.c_str(); }
 
+int eidm_last_dispatch(eidm_dispatch* out) {
+    if (!out) return api_fail(EIDM_E_INVALID, "dispatch receipt is NULL");
+    if (out->struct_size != sizeof(eidm_dispatch))
+        return api_fail(EIDM_E_INVALID, "dispatch.struct_size is %u, expected %zu", out->struct_size,
+                        sizeof(eidm_dispatch));
+    *out = g_receipt;
+    out->struct_size = sizeof(eidm_dispatch);
+    return ok();
+}
+
 int eidm_query(const eidm_shape* shape, int route, eidm_requirements* out) {
     if (!out) return api_fail(EIDM_E_INVALID, "requirements is NULL");
     if (out->struct_size != sizeof(eidm_requirements))
@@ -312,6 +352,7 @@ uint64_t eidm_map_scratch_bytes(uint32_t m, uint32_t top_k, uint32_t n_experts) 
 
 int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,
                     uint32_t top_k, int renormalize, uint32_t* ids, float* gates, void* stream) {
+    eidm::ReceiptScope receipt;
     int rc = check_route_args(logits, m, n_experts, top_k, ids, gates);
     if (rc) return rc;
     if (bias && !aligned(bias, 4)) return api_fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
@@ -323,6 +364,7 @@ int eidm_route_topk(const float* logits, const float* bias, uint32_t m, uint32_t
 
 int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts, uint32_t* counts,
              uint32_t* offsets, uint32_t* rows, void* scratch, uint64_t scratch_bytes, void* stream) {
+    eidm::ReceiptScope receipt;
     if (!ids || !counts || !offsets || !rows) return api_fail(EIDM_E_INVALID, "a map buffer is NULL");
     if (!m || !top_k || !n_experts) return api_fail(EIDM_E_INVALID, "zero dimension");
     if (n_experts > eidm::kMaxExperts)
@@ -346,6 +388,7 @@ int eidm_map(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts
 
 int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t n_experts,
                       int multiplicity, int32_t* bad_index_out, void* stream) {
+    eidm::ReceiptScope receipt;
     static std::mutex serial;  // the kernel reports through one device word
     if (!ids || !bad_index_out) return api_fail(EIDM_E_INVALID, "ids or bad_index_out is NULL");
     if (!m || !top_k || !n_experts) return api_fail(EIDM_E_INVALID, "zero dimension");
@@ -373,6 +416,7 @@ int eidm_validate_ids(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_t 
 int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint64_t weight_bytes,
                    const float* input, const uint32_t* ids, float* output, void* scratch,
                    uint64_t scratch_bytes, void* stream, int* route_taken) {
+    eidm::ReceiptScope receipt;
     eidm::MatmulArgs args{};
     eidm::MapBuffers buf{};
     int chosen = 0;
@@ -381,6 +425,7 @@ int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint
     if (rc) return rc;
     rc = run_matmul(args, buf, chosen, static_cast<hipStream_t>(stream));
     if (rc) return rc;
+    eidm::receipt_route(chosen);
     if (route_taken) *route_taken = chosen;
     return ok();
 }
@@ -404,6 +449,7 @@ int matmul_id_shared_map(const eidm_shape* shape, int route, const void* weights
     const bool grouped = chosen == EIDM_ROUTE_GROUPED;
     rc = run_matmul(args, buf, chosen, stream, !(grouped && *map_ready));
     if (rc) return rc;
+    receipt_route(chosen);
     if (grouped) *map_ready = true;
     if (route_taken) *route_taken = chosen;
     return ok();
@@ -415,6 +461,7 @@ extern "C" {
 
 int eidm_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y, const float* gates,
                  float* out, void* stream) {
+    eidm::ReceiptScope receipt;
     int rc = check_combine_args(m, top_k, n, y, gates, out);
     if (rc) return rc;
     hipError_t err = eidm::launch_combine(m, top_k, n, y, gates, out, static_cast<hipStream_t>(stream));
@@ -426,15 +473,17 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
                      const float* input, const float* logits, const float* bias, int renormalize,
                      uint32_t* ids, float* gates, float* y, float* out, void* scratch,
                      uint64_t scratch_bytes, void* stream, int* route_taken) {
-    if (shape && shape->id_multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN)
-        return api_fail(EIDM_E_INVALID, "the router produces distinct ids; use DISTINCT_PER_TOKEN");
-    if (!gates) return api_fail(EIDM_E_INVALID, "gates is NULL");
+    eidm::ReceiptScope receipt;
     eidm::MatmulArgs args{};
     eidm::MapBuffers buf{};
     int chosen = 0;
+    // prepare_matmul checks shape (struct_size first) before any field is read
     int rc = prepare_matmul(shape, route, weights, weight_bytes, input, ids, y, scratch,
                             scratch_bytes, &args, &buf, &chosen);
     if (rc) return rc;
+    if (shape->id_multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN)
+        return api_fail(EIDM_E_INVALID, "the router produces distinct ids; use DISTINCT_PER_TOKEN");
+    if (!gates) return api_fail(EIDM_E_INVALID, "gates is NULL");
     rc = check_route_args(logits, shape->m, shape->n_experts, shape->top_k, ids, gates);
     if (rc) return rc;
     if (bias && !aligned(bias, 4)) return api_fail(EIDM_E_ALIGN, "bias must be 4-byte aligned");
@@ -445,6 +494,7 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
         // one kernel: route, Direct matmul and combine per (token, column group)
         const hipError_t err = eidm::launch_moe_direct(args, logits, bias, renormalize, ids, gates, out, device_cus(), st);
         if (err != hipSuccess) return device_fail(err, "fused route/Direct/combine launch");
+        eidm::receipt_route(chosen);
         if (route_taken) *route_taken = chosen;
         return ok();
     }
@@ -455,6 +505,7 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
     if (rc) return rc;
     err = eidm::launch_combine(shape->m, shape->top_k, shape->n, y, gates, out, st);
     if (err != hipSuccess) return device_fail(err, "combine launch");
+    eidm::receipt_route(chosen);
     if (route_taken) *route_taken = chosen;
     return ok();
 }

@@ -44,6 +44,22 @@ uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts);
 int api_fail(int code, const char* fmt, ...);
 int api_ok();
 
+// The dispatch receipt (see eidm_last_dispatch): each public entry point
+// starts a new one on the calling thread; every kernel launch is noted.
+// The outermost scope on a thread starts the receipt; nested entry points
+// (a library call made by another one) add to it.
+struct ReceiptScope {
+    ReceiptScope();
+    ~ReceiptScope();
+    ReceiptScope(const ReceiptScope&) = delete;
+    ReceiptScope& operator=(const ReceiptScope&) = delete;
+};
+void receipt_route(int route);
+void note_launch(int kernel, uint32_t grid, uint32_t block, uint32_t lds_bytes);
+// hipGetLastError() after a launch; the launch goes on the receipt only when
+// it was accepted.
+hipError_t launched(int kernel, uint32_t grid, uint32_t block, uint32_t lds_bytes);
+
 hipError_t launch_route(const float* logits, const float* bias, uint32_t m, uint32_t n_experts,
                         uint32_t top_k, int renormalize, uint32_t* ids, float* gates,
                         hipStream_t stream);

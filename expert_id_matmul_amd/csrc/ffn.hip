@@ -114,6 +114,7 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
                  const float* logits, const float* bias, int renormalize, uint32_t* ids, float* gates,
                  float* out, void* scratch, uint64_t scratch_bytes, void* stream, int* route_taken) {
     using eidm::api_fail;
+    eidm::ReceiptScope dispatch_receipt;
     eidm::FfnLayout l{};
     eidm_shape gu{}, dn{};
     int rc = eidm::ffn_layout(shape, route, &l, &gu, &dn);
@@ -176,13 +177,14 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(eidm::silu_mul_kernel, dim3((uint32_t)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), g, u, count);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = eidm::launched(EIDM_KERNEL_SILU_MUL, (uint32_t)blocks, 256, 0);
     if (err != hipSuccess) return api_fail(EIDM_E_DEVICE, "silu * up launch: %s", hipGetErrorString(err));
     rc = eidm::matmul_id_shared_map(&dn, route, w_down, down_bytes, g, ids, y, grouped, l.grouped_bytes, st,
                                     &map_ready, nullptr);
     if (rc) return rc;
     rc = eidm_combine(shape->m, shape->top_k, shape->hidden, y, gates, out, stream);
     if (rc) return rc;
+    eidm::receipt_route(taken);
     if (route_taken) *route_taken = taken;
     return eidm::api_ok();
 }

@@ -247,7 +247,7 @@ hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_expe
         const uint32_t span = (per_wave + 63) / 64 * 64;  // <= 64 * kMapKeyedChunks
         hipLaunchKernelGGL(map_keyed_kernel, dim3(n_experts + 1), dim3(64 * kMapKeyedWaves), 0, stream, ids,
                            routed_rows, n_experts, span, buf.counts, buf.offsets, buf.rows);
-        return hipGetLastError();
+        return launched(EIDM_KERNEL_MAP_ONE_PASS, n_experts + 1, 64 * kMapKeyedWaves, 0);
     }
     const uint32_t waves = map_waves(n_experts);
     const uint32_t blocks = map_blocks(routed_rows, n_experts);
@@ -255,13 +255,13 @@ hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_expe
     const int nbits = key_bits(n_experts);
     hipLaunchKernelGGL(map_hist_kernel, dim3(blocks), dim3(64 * waves), buckets * sizeof(uint32_t),
                        stream, ids, routed_rows, n_experts, nbits, buf.hist);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launched(EIDM_KERNEL_MAP_HISTOGRAM, blocks, 64 * waves, buckets * sizeof(uint32_t));
     if (err != hipSuccess) return err;
     const size_t lds = ((2 + waves) * (size_t)buckets + waves) * sizeof(uint32_t);
     hipLaunchKernelGGL(map_scatter_kernel, dim3(blocks), dim3(64 * waves), lds, stream, ids,
                        routed_rows, n_experts, nbits, blocks, buf.hist, buf.counts, buf.offsets,
                        buf.rows);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_MAP_SCATTER, blocks, 64 * waves, (uint32_t)lds);
 }
 
 }  // namespace eidm

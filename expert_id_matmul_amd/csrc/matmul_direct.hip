@@ -67,11 +67,12 @@ template <int DT, int C, int WAVES, int D>
 hipError_t launch_cfg(const MatmulArgs& a, hipStream_t stream) {
     const uint32_t cols_per_block = 4 * C * WAVES;
     const dim3 grid(((a.n + cols_per_block - 1) / cols_per_block) * (a.m * a.top_k));
-    if (a.vec && direct_xstage_fits(a.k, 64 * WAVES))
+    const bool xs = a.vec && direct_xstage_fits(a.k, 64 * WAVES);
+    if (xs)
         hipLaunchKernelGGL((direct_kernel<DT, C, WAVES, D, true>), grid, dim3(64 * WAVES), (size_t)a.k * 4, stream, a);
     else
         hipLaunchKernelGGL((direct_kernel<DT, C, WAVES, D, false>), grid, dim3(64 * WAVES), 0, stream, a);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_DIRECT, grid.x, 64 * WAVES, xs ? a.k * 4 : 0);
 }
 
 template <int DT>

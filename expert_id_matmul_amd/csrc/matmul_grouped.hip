@@ -914,7 +914,8 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     grid = (grid + kXcds - 1) / kXcds * kXcds;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(64 * WAVES), lds, stream, a, buf.counts,
                        buf.offsets, buf.rows);
-    return hipGetLastError();
+    return launched(stream_form ? EIDM_KERNEL_GROUPED_STREAM : EIDM_KERNEL_GROUPED_JOB, (uint32_t)grid, 64 * WAVES,
+                    (uint32_t)lds);
 }
 
 // Tile shape per weight type.  16-bit weights: BM = 16 rows x BN = 128

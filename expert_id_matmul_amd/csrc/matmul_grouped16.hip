@@ -496,7 +496,7 @@ hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int devi
     grid = (grid + kG16Xcds - 1) / kG16Xcds * kG16Xcds;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kG16Threads), lds, stream, a, buf.counts, buf.offsets,
                        buf.rows);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_GROUPED_16X16, (uint32_t)grid, kG16Threads, (uint32_t)lds);
 }
 
 }  // namespace eidm

@@ -140,13 +140,14 @@ hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bia
     constexpr int D = moe_depth<DT, MAXW>();
     // with one activation row per token, the block's wavefronts share it
     // through LDS when they can stage it in one pass
-    if (a.layout == 0 && a.vec && direct_xstage_fits(a.k, 64 * a.top_k))
+    const bool xs = a.layout == 0 && a.vec && direct_xstage_fits(a.k, 64 * a.top_k);
+    if (xs)
         hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true>), grid, dim3(64 * a.top_k),
                            (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb);
     else
         hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false>), grid, dim3(64 * a.top_k), 0,
                            stream, a, logits, bias, renormalize, ids, gates, out, cb);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_FUSED_DECODE, grid.x, 64 * a.top_k, xs ? a.k * 4 : 0);
 }
 
 template <int DT>

@@ -52,6 +52,7 @@ int static_scratch(void** out) {
 extern "C" int eidm_matmul_id_noalloc(const eidm_shape* shape, int route, const void* weights,
                                       uint64_t weight_bytes, const float* input, const uint32_t* ids,
                                       float* output, void* stream, int* route_taken) {
+    eidm::ReceiptScope dispatch_receipt;
     eidm_requirements req{};
     req.struct_size = sizeof(req);
     int rc = eidm_query(shape, route == EIDM_ROUTE_AUTO ? EIDM_ROUTE_GROUPED : route, &req);

@@ -32,7 +32,7 @@ hipError_t launch_nv(const float* logits, const float* bias, uint32_t m, uint32_
     const dim3 grid((m + 3) / 4);
     hipLaunchKernelGGL(route_kernel<NV>, grid, dim3(256), 0, stream, logits, bias, m, n_experts,
                        top_k, renormalize, ids, gates);
-    return hipGetLastError();
+    return launched(EIDM_KERNEL_ROUTE, grid.x, 256, 0);
 }
 
 }  // namespace

@@ -54,7 +54,7 @@ hipError_t run_validate(const uint32_t* ids, uint32_t m, uint32_t top_k, uint32_
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(validate_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, ids, m, top_k,
                        n_experts, distinct);
-    err = hipGetLastError();
+    err = launched(EIDM_KERNEL_VALIDATE, (uint32_t)blocks, 256, 0);
     if (err != hipSuccess) return err;
     int result = none;
     err = hipMemcpyFromSymbolAsync(&result, HIP_SYMBOL(g_first_bad), sizeof(int), 0,

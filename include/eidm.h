@@ -33,8 +33,13 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously on it; nothing synchronises.
  *   - All arguments are validated on the host before anything is enqueued.
- *     On any error the call returns a negative eidm_status, enqueues
- *     nothing, and eidm_last_error() describes the failure.
+ *     On a validation error the call returns a negative eidm_status,
+ *     enqueues nothing, and eidm_last_error() describes the failure.  A
+ *     call of several steps (eidm_moe_forward, eidm_moe_ffn, a Grouped
+ *     eidm_matmul_id) that gets EIDM_E_DEVICE from a later launch has
+ *     already enqueued its earlier steps; its outputs (ids, gates, y,
+ *     out) are then undefined, and eidm_last_dispatch() lists what was
+ *     enqueued.
  *   - Sizes use overflow-checked products (an overflow is EIDM_E_INVALID).
  *   - Entry points are reentrant; a scratch buffer belongs to one call in
  *     flight at a time.
@@ -52,7 +57,7 @@
 extern "C" {
 #endif
 
-#define EIDM_ABI_VERSION 1
+#define EIDM_ABI_VERSION 2
 
 /* Native weight scalar type (DenseMatmulIdShape.weight_dtype). */
 typedef enum eidm_dtype {
@@ -125,6 +130,58 @@ typedef struct eidm_requirements {
     int32_t grouped_legal;       /* 1 when the Grouped route accepts the shape  */
     int32_t reserved0;
 } eidm_requirements;
+
+/* Kernels a call can launch (eidm_launch.kernel). */
+typedef enum eidm_kernel {
+    EIDM_KERNEL_ROUTE = 1,          /* sigmoid + bias top-k router                  */
+    EIDM_KERNEL_MAP_ONE_PASS = 2,   /* id -> row map, one launch (small maps)        */
+    EIDM_KERNEL_MAP_HISTOGRAM = 3,  /* id -> row map, first of two launches          */
+    EIDM_KERNEL_MAP_SCATTER = 4,    /* id -> row map, second of two launches         */
+    EIDM_KERNEL_DIRECT = 5,         /* Direct matmul_id                              */
+    EIDM_KERNEL_GROUPED_16X16 = 6,  /* Grouped matmul_id, 16x16x1 matrix-core form   */
+    EIDM_KERNEL_GROUPED_STREAM = 7, /* Grouped matmul_id, 4x4x1 streamed form        */
+    EIDM_KERNEL_GROUPED_JOB = 8,    /* Grouped matmul_id, 4x4x1 per-job form         */
+    EIDM_KERNEL_COMBINE = 9,        /* gate-weighted slot sum                        */
+    EIDM_KERNEL_FUSED_DECODE = 10,  /* route + Direct + combine in one launch        */
+    EIDM_KERNEL_SILU_MUL = 11,      /* expert FFN: silu(gate) * up                   */
+    EIDM_KERNEL_VALIDATE = 12,      /* id table check                                */
+    EIDM_KERNEL_PROOF = 13          /* calibration proof check                       */
+} eidm_kernel;
+
+/* One kernel launch: which kernel and its launch geometry (1-D grid of
+ * `grid` blocks of `block` threads, `lds_bytes` of dynamic LDS). */
+typedef struct eidm_launch {
+    int32_t kernel;                 /* eidm_kernel */
+    uint32_t grid;
+    uint32_t block;
+    uint32_t lds_bytes;
+} eidm_launch;
+
+#define EIDM_MAX_RECORDED_LAUNCHES 16
+
+/* What the calling thread's last call enqueued (mlx-native
+ * dense_matmul_id_auto.rs: the primitive's receipt {route, dispatch count}
+ * and fn expected_dispatches, the launch geometry checked after each
+ * encode). */
+typedef struct eidm_dispatch {
+    uint32_t struct_size;           /* set by the caller: sizeof(eidm_dispatch)         */
+    int32_t route;                  /* eidm_route the call ran (0: none, or it failed)   */
+    uint32_t dispatch_count;        /* kernel launches the call enqueued                 */
+    uint32_t recorded;              /* entries of launches[] filled, in launch order     */
+    eidm_launch launches[EIDM_MAX_RECORDED_LAUNCHES];
+} eidm_dispatch;
+
+/*
+ * Host-only: the dispatch receipt of the last library call on the calling
+ * thread (every entry point that can enqueue work starts a new one; calls a
+ * library entry point makes internally add to the caller's).  A successful
+ * eidm_matmul_id is 1 launch for Direct; for Grouped the map (1 or 2
+ * launches) and the Grouped kernel, or the Grouped kernel alone when the
+ * map is reused (the later projections of eidm_moe_ffn).  An
+ * eidm_moe_forward that runs Direct with top_k <= 16 is 1 fused launch.
+ * Enqueues nothing.
+ */
+int eidm_last_dispatch(eidm_dispatch* out);
 
 /* ABI version of the loaded library (EIDM_ABI_VERSION it was built with). */
 int eidm_abi_version(void);
@@ -317,12 +374,14 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
  * dense_matmul_id_auto.rs: fn calibration_buffers, fn calibrate_one_inner
  * and its winner rule, fn resolve_dense_matmul_id_auto_route).
  *
- * eidm_calibrate runs, for one exact shape and the caller's weights, on each
- * of two routing profiles (balanced ids (t+s) mod n_experts; skewed ids
- * s mod n_experts) with the page's adversarial activations:
+ * eidm_calibrate takes, for one exact shape and the caller's weights, a
+ * shape Grouped cannot run straight to Direct (no GPU work).  Otherwise it
+ * runs, on each of two routing profiles with the page's adversarial
+ * activations -- DISTINCT_PER_TOKEN shapes: balanced ids (t+s) mod n_experts
+ * and skewed ids s; MAY_REPEAT shapes: ids t mod n_experts for both --
  *   1. a Direct proof and a Grouped proof on poisoned outputs with a guard:
- *      every output must be overwritten, the guard untouched, and Grouped's
- *      bits equal to Direct's;
+ *      every output must be overwritten with a finite value, the guard
+ *      untouched, and Grouped's bits equal to Direct's;
  *   2. five timing rounds, alternating which form runs first; each call is
  *      timed by the host clock around launch + synchronisation (wall) and by
  *      HIP events on `stream` (GPU).
@@ -332,6 +391,18 @@ int eidm_moe_ffn(const eidm_ffn_shape* shape, int route, const void* w_gate, con
  * (percentiles of 5 sorted samples v: v[1], v[2], v[3]).  A failed Direct
  * proof aborts (EIDM_E_DEVICE); any Grouped failure or difference keeps
  * Direct.  The decision is stored in the plan for the exact shape.
+ *
+ * Activation limits (DenseMatmulIdCalibrationLimits, fail-closed): a plan
+ * counts, from eidm_plan_create (or eidm_plan_set_limits) on, the elapsed
+ * time, the distinct shapes calibrated (cases) and the host waits on the GPU
+ * (submissions: 1 for the inputs, then per profile 3 for the proofs and 10
+ * for the timing samples; 27 for a shape Grouped can run).  Calibrating a
+ * new shape beyond max_cases fails (EIDM_E_INVALID, nothing stored).  A
+ * shape whose complete gate the remaining submissions cannot cover, or that
+ * starts after the deadline, takes Direct without GPU work; a deadline that
+ * passes during the proofs or timing, or before the route is chosen, also
+ * gives Direct (reason EIDM_CAL_BUDGET).  eidm_plan_freeze after the
+ * deadline turns every Grouped entry of the plan into Direct.
  * Synchronous; not capturable in a graph; the workspace belongs to the call.
  */
 typedef struct eidm_plan eidm_plan; /* opaque; host memory owned by the library */
@@ -343,8 +414,19 @@ typedef enum eidm_calibration_reason {
     EIDM_CAL_NOT_IDENTICAL = 3,     /* Grouped's bits differ from Direct's */
     EIDM_CAL_WALL_MEDIAN = 4,       /* median wall time above 0.95 x Direct's */
     EIDM_CAL_WALL_QUARTILES = 5,    /* 75th-percentile wall not below Direct's 25th */
-    EIDM_CAL_GPU_MEDIAN = 6         /* median GPU time above 1.02 x Direct's */
+    EIDM_CAL_GPU_MEDIAN = 6,        /* median GPU time above 1.02 x Direct's */
+    EIDM_CAL_BUDGET = 7             /* the activation limits left no complete gate */
 } eidm_calibration_reason;
+
+/* Activation limits of a plan; every field nonzero.  Defaults: 15000 ms,
+ * 256 cases, 6145 submissions. */
+typedef struct eidm_calibration_limits {
+    uint32_t struct_size;     /* set to sizeof(eidm_calibration_limits) by the caller */
+    uint32_t max_cases;       /* distinct shapes the plan may calibrate */
+    uint32_t max_submissions; /* host waits on the GPU over all calibrations of the plan */
+    uint32_t reserved0;
+    uint64_t max_elapsed_ms;  /* wall time from the limits' start to eidm_plan_freeze */
+} eidm_calibration_limits;
 
 typedef struct eidm_calibration {
     uint32_t struct_size;  /* set to sizeof(eidm_calibration) by the caller */
@@ -352,7 +434,7 @@ typedef struct eidm_calibration {
     int32_t grouped_legal; /* Grouped could run the shape */
     int32_t bit_identical; /* Grouped reproduced Direct's bits on both profiles */
     int32_t reason;        /* eidm_calibration_reason */
-    int32_t reserved0;
+    uint32_t submissions;  /* host waits on the GPU this call made */
     /* per profile (0 balanced, 1 skewed), microseconds over 5 samples;
      * the grouped_* fields are 0 when Grouped did not run */
     double direct_wall_p25[2], direct_wall_median[2], direct_wall_p75[2], direct_gpu_median[2];
@@ -363,6 +445,10 @@ typedef struct eidm_calibration {
  * eidm_plan_destroy.  A plan may be shared by threads. */
 eidm_plan* eidm_plan_create(void);
 void eidm_plan_destroy(eidm_plan* plan);
+
+/* Replace the plan's activation limits and restart its clock; only before
+ * its first eidm_calibrate (else EIDM_E_INVALID, as for a zero limit). */
+int eidm_plan_set_limits(eidm_plan* plan, const eidm_calibration_limits* limits);
 
 /* Host-only: device workspace bytes eidm_calibrate needs for the shape (0 if
  * the shape is invalid).  The workspace must be 256-byte aligned. */
@@ -375,8 +461,10 @@ uint64_t eidm_calibration_workspace_bytes(const eidm_shape* shape);
 int eidm_calibrate(eidm_plan* plan, const eidm_shape* shape, const void* weights, uint64_t weight_bytes,
                    void* workspace, uint64_t workspace_bytes, void* stream, eidm_calibration* receipt);
 
-/* No further calibration; lookups keep working. */
-int eidm_plan_freeze(eidm_plan* plan);
+/* No further calibration; lookups keep working.  After the activation
+ * deadline every Grouped entry becomes Direct first.  downgraded (may be
+ * NULL) receives how many entries that changed. */
+int eidm_plan_freeze(eidm_plan* plan, uint32_t* downgraded);
 
 /* Host-only lookup: an exact calibrated shape gives its stored route; a
  * shape equal to a calibrated one in everything but m gives Direct;

@@ -29,12 +29,16 @@ def test_header_declares_what_the_binding_uses():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib.lib, name), name
-    assert lib.abi_version() == 1
+    assert lib.abi_version() == 2
 
 
 def test_struct_sizes_match_the_header_layout():
     assert ctypes.sizeof(B.Shape) == 48
     assert ctypes.sizeof(B.Requirements) == 56
+    assert ctypes.sizeof(B.Launch) == 16
+    assert ctypes.sizeof(B.Dispatch) == 16 + 16 * B.MAX_RECORDED_LAUNCHES
+    assert ctypes.sizeof(B.CalibrationLimits) == 24
+    assert ctypes.sizeof(B.Calibration) == 24 + 8 * 2 * 8
 
 
 def test_query_reports_the_pages_weight_extent_and_sizes(lib):
@@ -207,7 +211,7 @@ def test_calibration_struct_and_plan_rules_on_the_host(lib):
     rec.struct_size = ctypes.sizeof(B.Calibration)
     bad = B.make_shape(B.BF16, 0, 128, 256, 4, 16, 128 * 256 * 2, B.SHARED_PER_TOKEN, B.DISTINCT_PER_TOKEN)
     assert L.eidm_calibration_workspace_bytes(ctypes.byref(bad)) == 0
-    assert L.eidm_plan_freeze(plan) == B.OK
+    assert L.eidm_plan_freeze(plan, None) == B.OK
     assert L.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec)) == B.E_INVALID
     L.eidm_plan_destroy(plan)
 
@@ -242,3 +246,129 @@ def test_moe_ffn_rejects_bad_arguments_before_launch(lib):
     bad = B.FfnShape.from_buffer_copy(s)
     bad.n_experts, bad.top_k = 4096, 65  # past the router's limits
     assert L.eidm_moe_ffn(*args(shape=bad, gub=4096 * 32 * 64 * 2, db=4096 * 32 * 64 * 2)) == B.E_UNSUPPORTED
+
+
+def test_dispatch_receipt_rules_and_a_rejected_call_enqueues_nothing(lib):
+    """eidm_last_dispatch (mlx-native dense_matmul_id_auto.rs: the primitive's
+    receipt): a call rejected on the host reports no route and no launch."""
+    L = lib.lib
+    assert L.eidm_last_dispatch(None) == B.E_INVALID
+    d = B.Dispatch()
+    d.struct_size = 8
+    assert L.eidm_last_dispatch(ctypes.byref(d)) == B.E_INVALID
+    s = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2)
+    P = ctypes.c_void_p
+    # NULL output: rejected before anything is enqueued
+    assert L.eidm_matmul_id(ctypes.byref(s), B.DIRECT, P(FAKE), 16 * 128 * 256 * 2, P(FAKE), P(FAKE), None,
+                            None, 0, None, None) == B.E_INVALID
+    d = lib.last_dispatch()
+    assert (d.route, d.dispatch_count, d.recorded) == (0, 0, 0)
+    assert d.struct_size == ctypes.sizeof(B.Dispatch)
+
+
+def _cal_args(lib, s):
+    need = lib.lib.eidm_calibration_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    rec = B.Calibration()
+    rec.struct_size = ctypes.sizeof(B.Calibration)
+    wb = s.n_experts * s.expert_stride_bytes
+    return need, rec, wb
+
+
+def _calibrate_no_gpu(lib, plan, s):
+    """eidm_calibrate on fake addresses: only paths that enqueue nothing may
+    run here (the budget and case rules are decided before any GPU work)."""
+    need, rec, wb = _cal_args(lib, s)
+    P = ctypes.c_void_p
+    rc = lib.lib.eidm_calibrate(plan, ctypes.byref(s), P(FAKE), wb, P(FAKE), need, None, ctypes.byref(rec))
+    return rc, rec
+
+
+def _limits(ms, cases, subs, size=None):
+    lim = B.CalibrationLimits(ctypes.sizeof(B.CalibrationLimits) if size is None else size, cases, subs, 0, ms)
+    return ctypes.byref(lim)
+
+
+def test_calibration_limits_must_be_nonzero_and_precede_calibration(lib):
+    """DenseMatmulIdCalibrationLimits: every limit nonzero; the limits are fixed
+    once calibration has begun."""
+    L = lib.lib
+    plan = L.eidm_plan_create()
+    try:
+        assert L.eidm_plan_set_limits(None, _limits(1, 1, 1)) == B.E_INVALID
+        assert L.eidm_plan_set_limits(plan, None) == B.E_INVALID
+        assert L.eidm_plan_set_limits(plan, _limits(1, 1, 1, size=16)) == B.E_INVALID
+        for ms, cases, subs in ((0, 1, 1), (1, 0, 1), (1, 1, 0)):
+            assert L.eidm_plan_set_limits(plan, _limits(ms, cases, subs)) == B.E_INVALID
+        assert "nonzero" in lib.last_error()
+        assert L.eidm_plan_set_limits(plan, _limits(15000, 256, B.GATE_SUBMISSIONS - 1)) == B.OK
+        s = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2)
+        rc, rec = _calibrate_no_gpu(lib, plan, s)
+        assert rc == B.OK
+        assert L.eidm_plan_set_limits(plan, _limits(15000, 256, 6145)) == B.E_INVALID
+    finally:
+        L.eidm_plan_destroy(plan)
+
+
+def test_calibration_without_budget_for_a_complete_gate_takes_direct(lib):
+    """fn calibrate_one_inner: a shape whose proofs and timing the remaining
+    submissions cannot pay for in full takes Direct with no GPU work."""
+    L = lib.lib
+    plan = L.eidm_plan_create()
+    try:
+        assert L.eidm_plan_set_limits(plan, _limits(15000, 256, B.GATE_SUBMISSIONS - 1)) == B.OK
+        s = B.make_shape(B.BF16, 512, 128, 256, 4, 16, 128 * 256 * 2)
+        rc, rec = _calibrate_no_gpu(lib, plan, s)
+        assert rc == B.OK
+        assert (rec.route, rec.reason, rec.submissions) == (B.DIRECT, B.CAL_BUDGET, 0)
+        assert rec.grouped_legal == 1 and rec.bit_identical == 0
+        assert list(rec.grouped_wall_median) == [0.0, 0.0]
+        route = ctypes.c_int(-1)
+        assert L.eidm_plan_route(plan, ctypes.byref(s), ctypes.byref(route)) == B.OK
+        assert route.value == B.DIRECT
+        assert lib.last_dispatch().dispatch_count == 0
+        n = ctypes.c_uint32(99)
+        assert L.eidm_plan_freeze(plan, ctypes.byref(n)) == B.OK and n.value == 0
+    finally:
+        L.eidm_plan_destroy(plan)
+
+
+def test_calibration_after_the_deadline_takes_direct(lib):
+    """The budget check before any proof: past max_elapsed_ms a shape takes
+    Direct; freezing after the deadline has no Grouped entry to downgrade."""
+    import time
+    L = lib.lib
+    plan = L.eidm_plan_create()
+    try:
+        assert L.eidm_plan_set_limits(plan, _limits(1, 256, 6145)) == B.OK
+        time.sleep(0.01)
+        s = B.make_shape(B.F16, 300, 64, 128, 2, 8, 64 * 128 * 2)
+        rc, rec = _calibrate_no_gpu(lib, plan, s)
+        assert rc == B.OK
+        assert (rec.route, rec.reason, rec.submissions) == (B.DIRECT, B.CAL_BUDGET, 0)
+        n = ctypes.c_uint32(99)
+        assert L.eidm_plan_freeze(plan, ctypes.byref(n)) == B.OK and n.value == 0
+    finally:
+        L.eidm_plan_destroy(plan)
+
+
+def test_calibration_case_limit_fails_closed(lib):
+    """validate_cases: more distinct shapes than max_cases is an error and
+    stores nothing; the same shape again is no new case."""
+    L = lib.lib
+    plan = L.eidm_plan_create()
+    try:
+        assert L.eidm_plan_set_limits(plan, _limits(15000, 2, 1)) == B.OK
+        a = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2)
+        b = B.make_shape(B.BF16, 65, 128, 256, 4, 16, 128 * 256 * 2)
+        c = B.make_shape(B.BF16, 64, 136, 256, 4, 16, 136 * 256 * 2)
+        for s in (a, a, b, a):
+            rc, rec = _calibrate_no_gpu(lib, plan, s)
+            assert rc == B.OK and rec.reason == B.CAL_BUDGET
+        rc, rec = _calibrate_no_gpu(lib, plan, c)
+        assert rc == B.E_INVALID
+        assert "2 cases" in lib.last_error()
+        route = ctypes.c_int(-1)
+        assert L.eidm_plan_route(plan, ctypes.byref(c), ctypes.byref(route)) == B.E_UNSUPPORTED
+    finally:
+        L.eidm_plan_destroy(plan)

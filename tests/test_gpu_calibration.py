@@ -84,3 +84,86 @@ def test_calibration_follows_the_rule_and_serves_the_plan(lib, name, m, n, k, to
         plan.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
     assert e.value.code == B.E_INVALID
     assert plan.route(shape) == rec.route
+
+
+def _section(ws, offset, count, dtype):
+    return ws[offset: offset + count * 4].cpu().numpy().view(dtype)
+
+
+def _layout(wl):
+    """Workspace sections of eidm_calibrate: activations, then the two id
+    tables, each at a 256-byte boundary."""
+    a = lambda v: (v + 255) // 256 * 256
+    x = 0
+    ids0 = a(x + wl.input_rows * wl.k * 4)
+    ids1 = a(ids0 + wl.routed_rows * 4)
+    return x, ids0, ids1
+
+
+@pytest.mark.parametrize("mult", [W.IDS_DISTINCT, W.IDS_MAY_REPEAT])
+def test_calibration_inputs_follow_the_page(lib, mult):
+    """fn calibration_buffers: the adversarial activations; distinct ids
+    calibrate on balanced (t+s) mod E and skewed s, ids that may repeat on
+    t mod E for both profiles.  One complete gate is 27 host waits."""
+    top_k, E = (6, 4) if mult == W.IDS_MAY_REPEAT else (4, 16)
+    print(f"[case] calibrate inputs mult={mult}", flush=True)
+    wl = W.Workload("cal_in", W.DT_BF16, 96, 128, 512, top_k, E, 128 * 512 * 2, W.LAYOUT_SHARED, mult, 81, 0.02,
+                    "random", "uniform")
+    weights = torch.empty(wl.weight_bytes, dtype=torch.uint8, device="cuda")
+    W.fill_weights(wl, weights)
+    plan = B.Plan(lib)
+    shape = B.shape_of(wl)
+    ws = torch.empty(plan.workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    rec = plan.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
+    torch.cuda.synchronize()
+    print("[case] receipt", rec.as_dict(), flush=True)
+    assert rec.grouped_legal == 1 and rec.bit_identical == 1
+    assert rec.reason not in (2, 3, B.CAL_BUDGET)
+    assert rec.submissions == B.GATE_SUBMISSIONS
+    assert rec.route == rule(rec)
+    x0, i0, i1 = _layout(wl)
+    x = _section(ws, x0, wl.input_rows * wl.k, np.float32).reshape(wl.input_rows, wl.k)
+    assert np.array_equal(x.view(np.uint32), W.adversarial_activations(wl.input_rows, wl.k).view(np.uint32))
+    t = np.arange(wl.m)[:, None]
+    s = np.arange(top_k)[None, :]
+    ids0 = _section(ws, i0, wl.routed_rows, np.uint32).reshape(wl.m, top_k)
+    ids1 = _section(ws, i1, wl.routed_rows, np.uint32).reshape(wl.m, top_k)
+    if mult == W.IDS_MAY_REPEAT:
+        want0 = want1 = np.broadcast_to(t % E, (wl.m, top_k))
+    else:
+        want0 = (t + s) % E
+        want1 = np.broadcast_to(s, (wl.m, top_k))
+    assert np.array_equal(ids0, want0) and np.array_equal(ids1, want1)
+
+
+def test_submission_budget_and_deadline_downgrade(lib):
+    """Budget rules on the GPU: a plan with room for exactly one gate
+    calibrates one shape and gives the next Direct without GPU work; a plan
+    frozen after its deadline turns its Grouped entries into Direct
+    (fn downgrade_grouped_after_deadline)."""
+    import time
+    # many routed rows over few experts: Grouped reads each expert's weights once
+    wl, weights, plan, shape, ws = _setup(lib, W.DT_BF16, 2048, 512, 1024, 8, 64, seed=82)
+    print("[case] calibrate budget", flush=True)
+    plan.set_limits(max_elapsed_ms=60000, max_cases=4, max_submissions=B.GATE_SUBMISSIONS)
+    rec = plan.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
+    print("[case] receipt", rec.as_dict(), flush=True)
+    assert rec.submissions == B.GATE_SUBMISSIONS and rec.bit_identical == 1
+    assert rec.route == B.GROUPED, B.CAL_REASONS[rec.reason]
+    other = B.shape_of(wl.with_(m=1024))
+    rec2 = plan.calibrate(other, weights, ws, weight_bytes=wl.weight_bytes)
+    assert (rec2.route, rec2.reason, rec2.submissions) == (B.DIRECT, B.CAL_BUDGET, 0)
+    assert plan.freeze() == 0  # before the deadline: nothing changes
+    assert plan.route(shape) == B.GROUPED
+
+    plan2 = B.Plan(lib)
+    deadline_ms = 3000
+    plan2.set_limits(max_elapsed_ms=deadline_ms)
+    t0 = time.monotonic()
+    rec = plan2.calibrate(shape, weights, ws, weight_bytes=wl.weight_bytes)
+    assert rec.route == B.GROUPED, B.CAL_REASONS[rec.reason]
+    assert plan2.route(shape) == B.GROUPED
+    time.sleep(max(0.0, deadline_ms / 1000 + 0.1 - (time.monotonic() - t0)))
+    assert plan2.freeze() == 1
+    assert plan2.route(shape) == B.DIRECT
+    torch.cuda.synchronize()
