@@ -19,6 +19,7 @@ F32, F16, BF16 = 0, 1, 2
 SHARED_PER_TOKEN, SLOTTED = 0, 1
 DISTINCT_PER_TOKEN, MAY_REPEAT = 0, 1
 AUTO, DIRECT, GROUPED = 0, 1, 2
+ARITH_F32, ARITH_SPLIT16 = 0, 1
 OK, E_INVALID, E_UNSUPPORTED, E_SIZE, E_ALIGN, E_DEVICE, E_IDS = 0, -1, -2, -3, -4, -5, -6
 
 EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk", "eidm_map",
@@ -31,7 +32,8 @@ EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk
 # eidm_kernel (include/eidm.h): kernels a call can launch
 KERNELS = {1: "route", 2: "map_one_pass", 3: "map_histogram", 4: "map_scatter", 5: "direct",
            6: "grouped_16x16", 7: "grouped_stream", 8: "grouped_job", 9: "combine",
-           10: "fused_decode", 11: "silu_mul", 12: "validate", 13: "proof"}
+           10: "fused_decode", 11: "silu_mul", 12: "validate", 13: "proof", 14: "split_x",
+           15: "direct_split16", 16: "grouped_split16"}
 MAX_RECORDED_LAUNCHES = 16
 
 
@@ -39,7 +41,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("weight_dtype", ctypes.c_int32),
                 ("m", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
                 ("top_k", ctypes.c_uint32), ("n_experts", ctypes.c_uint32),
-                ("reserved0", ctypes.c_uint32), ("expert_stride_bytes", ctypes.c_uint64),
+                ("arith", ctypes.c_int32), ("expert_stride_bytes", ctypes.c_uint64),
                 ("input_layout", ctypes.c_int32), ("id_multiplicity", ctypes.c_int32)]
 
 
@@ -121,15 +123,16 @@ class EidmError(RuntimeError):
 
 
 def make_shape(dtype: int, m: int, n: int, k: int, top_k: int, n_experts: int, stride: int,
-               layout: int = SHARED_PER_TOKEN, multiplicity: int = DISTINCT_PER_TOKEN) -> Shape:
-    return Shape(ctypes.sizeof(Shape), dtype, m, n, k, top_k, n_experts, 0, stride, layout,
+               layout: int = SHARED_PER_TOKEN, multiplicity: int = DISTINCT_PER_TOKEN,
+               arith: int = ARITH_F32) -> Shape:
+    return Shape(ctypes.sizeof(Shape), dtype, m, n, k, top_k, n_experts, arith, stride, layout,
                  multiplicity)
 
 
 def shape_of(wl) -> Shape:
     """Shape key of a workloads.Workload."""
     return make_shape(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout,
-                      wl.multiplicity)
+                      wl.multiplicity, wl.arith)
 
 
 def _nbytes(t) -> int:

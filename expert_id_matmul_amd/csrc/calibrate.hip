@@ -75,7 +75,7 @@ constexpr uint32_t kGateSubmissions = 1 + 2 * (3 + 2 * kTimingRounds);
 bool same_base(const eidm_shape& a, const eidm_shape& b) {
     return a.weight_dtype == b.weight_dtype && a.n == b.n && a.k == b.k && a.top_k == b.top_k &&
            a.n_experts == b.n_experts && a.expert_stride_bytes == b.expert_stride_bytes &&
-           a.input_layout == b.input_layout && a.id_multiplicity == b.id_multiplicity;
+           a.input_layout == b.input_layout && a.id_multiplicity == b.id_multiplicity && a.arith == b.arith;
 }
 
 bool same_shape(const eidm_shape& a, const eidm_shape& b) { return same_base(a, b) && a.m == b.m; }
@@ -101,7 +101,8 @@ int layout_for(const eidm_shape* shape, Layout* l) {
     l->input_elements = rd.input_elements;
     l->routed = rd.ids_elements;
     l->output_elements = rd.output_elements;
-    l->scratch_bytes = l->grouped_legal ? rg.scratch_bytes : 0;
+    // one scratch for both forms (the split-16 Direct form needs one too)
+    l->scratch_bytes = l->grouped_legal && rg.scratch_bytes > rd.scratch_bytes ? rg.scratch_bytes : rd.scratch_bytes;
     uint64_t off = 0;
     l->x = off;
     off = align256(off + l->input_elements * 4);
@@ -337,7 +338,7 @@ int eidm_calibrate(eidm_plan* plan, const eidm_shape* shape, const void* weights
     uint32_t* ids[2] = {reinterpret_cast<uint32_t*>(ws + l.ids0), reinterpret_cast<uint32_t*>(ws + l.ids1)};
     float* yd = reinterpret_cast<float*>(ws + l.yd);
     float* yg = reinterpret_cast<float*>(ws + l.yg);
-    void* scratch = ws + l.scratch;
+    void* scratch = ws + l.scratch;  // l.scratch_bytes of it
     unsigned long long* counters = reinterpret_cast<unsigned long long*>(ws + l.counters);
     const int may_repeat = shape->id_multiplicity == EIDM_IDS_MAY_REPEAT;
 
@@ -379,9 +380,8 @@ int eidm_calibrate(eidm_plan* plan, const eidm_shape* shape, const void* weights
         const auto t0 = std::chrono::steady_clock::now();
         hipError_t err = hipEventRecord(ev[0], st);
         if (err != hipSuccess) return hip_fail(err, "event record");
-        int r = eidm_matmul_id(shape, route, weights, weight_bytes, x, ids[p], y,
-                               route == EIDM_ROUTE_GROUPED ? scratch : nullptr,
-                               route == EIDM_ROUTE_GROUPED ? l.scratch_bytes : 0, stream, nullptr);
+        int r = eidm_matmul_id(shape, route, weights, weight_bytes, x, ids[p], y, l.scratch_bytes ? scratch : nullptr,
+                               l.scratch_bytes, stream, nullptr);
         if (r) return r;
         err = hipEventRecord(ev[1], st);
         if (err == hipSuccess) err = hipStreamSynchronize(st);

@@ -104,8 +104,10 @@ struct Plan {
     uint64_t output_elements = 0;
     uint64_t required_weight_bytes = 0;
     uint64_t grouped_scratch = 0;
-    // byte offsets of the grouped scratch sections
-    uint64_t off_hist = 0, off_counts = 0, off_offsets = 0, off_rows = 0;
+    uint64_t direct_scratch = 0;  // the split activations (SPLIT16), else 0
+    // byte offsets of the grouped scratch sections (the split activations
+    // follow the map; a Direct scratch holds them at offset 0)
+    uint64_t off_hist = 0, off_counts = 0, off_offsets = 0, off_rows = 0, off_split = 0;
 };
 
 int check_shape(const eidm_shape* s, Plan* p) {
@@ -119,7 +121,12 @@ int check_shape(const eidm_shape* s, Plan* p) {
         return api_fail(EIDM_E_INVALID, "unknown input layout %d", s->input_layout);
     if (s->id_multiplicity != EIDM_IDS_DISTINCT_PER_TOKEN && s->id_multiplicity != EIDM_IDS_MAY_REPEAT)
         return api_fail(EIDM_E_INVALID, "unknown id multiplicity %d", s->id_multiplicity);
-    if (s->reserved0 != 0) return api_fail(EIDM_E_INVALID, "shape.reserved0 must be 0");
+    if (s->arith != EIDM_ARITH_F32 && s->arith != EIDM_ARITH_SPLIT16)
+        return api_fail(EIDM_E_INVALID, "unknown arith %d", s->arith);
+    if (s->arith == EIDM_ARITH_SPLIT16 && size != 2)
+        return api_fail(EIDM_E_UNSUPPORTED, "the split-16 arithmetic needs 16-bit weights");
+    if (s->arith == EIDM_ARITH_SPLIT16 && s->k % 8 != 0)
+        return api_fail(EIDM_E_UNSUPPORTED, "the split-16 arithmetic needs k a multiple of 8 (k=%u)", s->k);
     if (!s->m || !s->n || !s->k || !s->top_k || !s->n_experts)
         return api_fail(EIDM_E_INVALID, "zero dimension (m=%u n=%u k=%u top_k=%u n_experts=%u)", s->m,
                     s->n, s->k, s->top_k, s->n_experts);
@@ -163,7 +170,15 @@ int check_shape(const eidm_shape* s, Plan* p) {
     p->off_counts = align256(eidm::map_hist_elements(routed, s->n_experts) * 4);
     p->off_offsets = p->off_counts + align256((uint64_t)(s->n_experts + 1) * 4);
     p->off_rows = p->off_offsets + align256((uint64_t)(s->n_experts + 2) * 4);
-    p->grouped_scratch = p->off_rows + align256(routed * 4);
+    p->off_split = p->off_rows + align256(routed * 4);
+    p->grouped_scratch = p->off_split;
+    if (s->arith == EIDM_ARITH_SPLIT16) {
+        uint64_t split;  // three 16-bit parts per input element
+        if (!mul_ok(in_el, 6, &split)) return api_fail(EIDM_E_INVALID, "split input size overflows");
+        p->direct_scratch = align256(split);
+        if (!add_ok(p->grouped_scratch, p->direct_scratch, &p->grouped_scratch))
+            return api_fail(EIDM_E_INVALID, "scratch size overflows");
+    }
     return EIDM_OK;
 }
 
@@ -224,8 +239,19 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
     if (!input || !ids || !output) return api_fail(EIDM_E_INVALID, "input, ids or output is NULL");
     if (!aligned(input, 4) || !aligned(ids, 4) || !aligned(output, 4))
         return api_fail(EIDM_E_ALIGN, "input, ids and output must be 4-byte aligned");
+    const bool split = s->arith == EIDM_ARITH_SPLIT16;
+    if (split && (!aligned(weights, 16) || s->expert_stride_bytes % 16 || !aligned(input, 16)))
+        return api_fail(EIDM_E_ALIGN, "the split-16 arithmetic needs weights, expert stride and input 16-byte aligned");
     rc = resolve_route(s, p, route, true, scratch ? scratch_bytes : 0, chosen);
     if (rc) return rc;
+    args->xsplit = nullptr;
+    if (split && *chosen == EIDM_ROUTE_DIRECT) {
+        if (!scratch || scratch_bytes < p.direct_scratch)
+            return api_fail(EIDM_E_SIZE, "the split-16 Direct route needs %llu bytes of scratch, got %llu",
+                            (unsigned long long)p.direct_scratch, (unsigned long long)(scratch ? scratch_bytes : 0));
+        if (!aligned(scratch, 256)) return api_fail(EIDM_E_ALIGN, "scratch must be 256-byte aligned");
+        args->xsplit = static_cast<uint16_t*>(scratch);
+    }
     if (*chosen == EIDM_ROUTE_GROUPED) {
         if (!scratch) return api_fail(EIDM_E_SIZE, "Grouped route needs %llu bytes of scratch, got none",
                                   (unsigned long long)p.grouped_scratch);
@@ -238,6 +264,7 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
         buf->counts = reinterpret_cast<uint32_t*>(base + p.off_counts);
         buf->offsets = reinterpret_cast<uint32_t*>(base + p.off_offsets);
         buf->rows = reinterpret_cast<uint32_t*>(base + p.off_rows);
+        if (split) args->xsplit = reinterpret_cast<uint16_t*>(base + p.off_split);
     }
     args->dtype = s->weight_dtype;
     args->m = s->m;
@@ -251,6 +278,7 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
     args->input = input;
     args->ids = ids;
     args->output = output;
+    args->arith = s->arith;
     args->vec = aligned(weights, 16) && s->expert_stride_bytes % 16 == 0 &&
                 ((uint64_t)s->k * size) % 16 == 0 && aligned(input, 16) && s->k % 4 == 0;
     return EIDM_OK;
@@ -260,6 +288,22 @@ int prepare_matmul(const eidm_shape* s, int route, const void* weights, uint64_t
 int run_matmul(const eidm::MatmulArgs& args, const eidm::MapBuffers& buf, int chosen,
                hipStream_t stream, bool build_map = true) {
     hipError_t err;
+    if (args.arith == EIDM_ARITH_SPLIT16) {
+        err = eidm::launch_split16_x(args, stream);
+        if (err != hipSuccess) return device_fail(err, "activation split launch");
+        if (chosen == EIDM_ROUTE_GROUPED) {
+            if (build_map) {
+                err = eidm::launch_map(args.ids, args.m * args.top_k, args.n_experts, buf, stream);
+                if (err != hipSuccess) return device_fail(err, "map launch");
+            }
+            err = eidm::launch_grouped_split16(args, buf, device_cus(), stream);
+            if (err != hipSuccess) return device_fail(err, "split-16 grouped launch");
+        } else {
+            err = eidm::launch_direct_split16(args, stream);
+            if (err != hipSuccess) return device_fail(err, "split-16 direct launch");
+        }
+        return EIDM_OK;
+    }
     if (chosen == EIDM_ROUTE_GROUPED) {
         if (build_map) {
             err = eidm::launch_map(args.ids, args.m * args.top_k, args.n_experts, buf, stream);
@@ -338,7 +382,7 @@ int eidm_query(const eidm_shape* shape, int route, eidm_requirements* out) {
     out->input_elements = p.input_elements;
     out->ids_elements = p.routed;
     out->output_elements = p.output_elements;
-    out->scratch_bytes = chosen == EIDM_ROUTE_GROUPED ? p.grouped_scratch : 0;
+    out->scratch_bytes = chosen == EIDM_ROUTE_GROUPED ? p.grouped_scratch : p.direct_scratch;
     out->grouped_legal = 1;
     out->reserved0 = 0;
     return ok();
@@ -490,7 +534,8 @@ int eidm_moe_forward(const eidm_shape* shape, int route, const void* weights, ui
     rc = check_combine_args(shape->m, shape->top_k, shape->n, y, gates, out);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (chosen == EIDM_ROUTE_DIRECT && eidm::moe_direct_supported(shape->top_k, shape->n_experts)) {
+    if (chosen == EIDM_ROUTE_DIRECT && shape->arith == EIDM_ARITH_F32 &&
+        eidm::moe_direct_supported(shape->top_k, shape->n_experts)) {
         // one kernel: route, Direct matmul and combine per (token, column group)
         const hipError_t err = eidm::launch_moe_direct(args, logits, bias, renormalize, ids, gates, out, device_cus(), st);
         if (err != hipSuccess) return device_fail(err, "fused route/Direct/combine launch");

@@ -26,6 +26,8 @@ struct MatmulArgs {
     const uint32_t* ids;
     float* output;
     bool vec;                   // 16-byte aligned rows: vector loads allowed
+    int arith;                  // eidm_arith
+    uint16_t* xsplit;           // SPLIT16: the split activations (scratch), else null
 };
 
 // Device pointers into a Grouped scratch buffer.
@@ -80,6 +82,11 @@ hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device
 // grouped16_supported says so.
 bool grouped16_supported(const MatmulArgs& a);
 hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
+// The split-16 arithmetic: the activation split (input -> a.xsplit), then
+// the Direct or the Grouped form.
+hipError_t launch_split16_x(const MatmulArgs& a, hipStream_t stream);
+hipError_t launch_direct_split16(const MatmulArgs& a, hipStream_t stream);
+hipError_t launch_grouped_split16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,
                           const float* gates, float* out, hipStream_t stream);
 bool moe_direct_supported(uint32_t top_k, uint32_t n_experts);

@@ -57,17 +57,17 @@ extern "C" int eidm_matmul_id_noalloc(const eidm_shape* shape, int route, const 
     req.struct_size = sizeof(req);
     int rc = eidm_query(shape, route == EIDM_ROUTE_AUTO ? EIDM_ROUTE_GROUPED : route, &req);
     if (rc) return rc;
-    if (route == EIDM_ROUTE_GROUPED && req.scratch_bytes > kStaticScratchBytes)
+    if (route != EIDM_ROUTE_AUTO && req.scratch_bytes > kStaticScratchBytes)
         return eidm::api_fail(EIDM_E_SIZE,
-                              "the Grouped route needs %llu bytes of scratch for this shape, above the %llu bytes "
+                              "the route needs %llu bytes of scratch for this shape, above the %llu bytes "
                               "of the library's static array",
                               (unsigned long long)req.scratch_bytes, (unsigned long long)kStaticScratchBytes);
     void* s = nullptr;
     uint64_t sbytes = 0;
-    if (route != EIDM_ROUTE_DIRECT) {
+    if (route != EIDM_ROUTE_DIRECT || req.scratch_bytes) {
         rc = static_scratch(&s);
         if (rc) return rc;
-        sbytes = kStaticScratchBytes;  // AUTO keeps Direct when the map would not fit
+        sbytes = kStaticScratchBytes;  // AUTO keeps Direct when Grouped's scratch would not fit
     }
     return eidm_matmul_id(shape, route, weights, weight_bytes, input, ids, output, s, sbytes, stream, route_taken);
 }

@@ -68,6 +68,7 @@ class Workload:
     w_std: float
     ids_kind: str
     gates_kind: str
+    arith: int = 0  # eidm_arith: 0 the f32 order, 1 the split-16 matrix-core order
 
     @property
     def routed_rows(self) -> int:

@@ -79,6 +79,18 @@ typedef enum eidm_multiplicity {
     EIDM_IDS_MAY_REPEAT = 1
 } eidm_multiplicity;
 
+/* The arithmetic of the matmul.  F32: native weights widened to f32, f32
+ * fma in the fixed 16-slice order (see eidm_matmul_id).  SPLIT16: 16-bit
+ * weights kept exact in their own type, each f32 activation split exactly
+ * into three parts of that type, products on the 16-bit matrix core (the
+ * value-independence theorem statement of dense_matmul_id_auto.rs: both
+ * routes, one order).  Both routes give identical bits within a mode; the
+ * modes differ from each other by rounding only. */
+typedef enum eidm_arith {
+    EIDM_ARITH_F32 = 0,
+    EIDM_ARITH_SPLIT16 = 1
+} eidm_arith;
+
 /* Which form of the matmul runs (DenseMatmulIdRoute, plus AUTO). */
 typedef enum eidm_route {
     EIDM_ROUTE_AUTO = 0,
@@ -101,8 +113,8 @@ typedef enum eidm_status {
  * dtype, m, n, k, top_k, n_experts, expert stride, input layout, id
  * multiplicity).  Expert e's weight matrix is [n, k], row-major (k
  * contiguous), starting at byte e * expert_stride_bytes of the weight
- * buffer; the stride may include padding.  struct_size must be
- * sizeof(eidm_shape).
+ * buffer; the stride may include padding.  `arith` picks the arithmetic
+ * (eidm_arith; 0 is the f32 order).  struct_size must be sizeof(eidm_shape).
  */
 typedef struct eidm_shape {
     uint32_t struct_size;
@@ -112,7 +124,7 @@ typedef struct eidm_shape {
     uint32_t k;                  /* reduction length           */
     uint32_t top_k;              /* routed rows per token      */
     uint32_t n_experts;
-    uint32_t reserved0;          /* must be 0                  */
+    int32_t arith;               /* eidm_arith (0: F32)        */
     uint64_t expert_stride_bytes;
     int32_t input_layout;        /* eidm_layout                */
     int32_t id_multiplicity;     /* eidm_multiplicity          */
@@ -145,7 +157,10 @@ typedef enum eidm_kernel {
     EIDM_KERNEL_FUSED_DECODE = 10,  /* route + Direct + combine in one launch        */
     EIDM_KERNEL_SILU_MUL = 11,      /* expert FFN: silu(gate) * up                   */
     EIDM_KERNEL_VALIDATE = 12,      /* id table check                                */
-    EIDM_KERNEL_PROOF = 13          /* calibration proof check                       */
+    EIDM_KERNEL_PROOF = 13,         /* calibration proof check                       */
+    EIDM_KERNEL_SPLIT_X = 14,       /* split-16: activations into three parts        */
+    EIDM_KERNEL_DIRECT_SPLIT16 = 15,  /* split-16 Direct                             */
+    EIDM_KERNEL_GROUPED_SPLIT16 = 16  /* split-16 Grouped                            */
 } eidm_kernel;
 
 /* One kernel launch: which kernel and its launch geometry (1-D grid of
@@ -254,11 +269,25 @@ uint64_t eidm_map_scratch_bytes(uint32_t m, uint32_t top_k, uint32_t n_experts);
  * scratch      device, >= scratch_bytes from eidm_query for the route (may
  *              be NULL for Direct); 256-byte aligned
  * route_taken  (optional host int*) receives the route that ran
- * Both routes give bit-identical outputs for the same inputs.  The
- * reduction over k is the same fixed order in both: k is cut into granules
- * of 8; granule g belongs to slice g mod 16; each slice accumulates its
- * products in ascending k with f32 fma from +0; the 16 slice sums are added
- * pairwise as (s, s+8), then (s, s+4), (s, s+2), (s, s+1).
+ * Both routes give bit-identical outputs for the same inputs.  With
+ * EIDM_ARITH_F32 the reduction over k is the same fixed order in both: k is
+ * cut into granules of 8; granule g belongs to slice g mod 16; each slice
+ * accumulates its products in ascending k with f32 fma from +0; the 16
+ * slice sums are added pairwise as (s, s+8), then (s, s+4), (s, s+2),
+ * (s, s+1).
+ * With EIDM_ARITH_SPLIT16 (16-bit weights; k a multiple of 8; weights,
+ * stride and input 16-byte aligned) each activation x is split into
+ * p1 = rn(x), p2 = rn(x - p1), p3 = rn(x - p1 - p2) in the weight type
+ * (exact for bf16; for f16, |x| must stay below 65504 and parts below
+ * 2^-24 round), and k is cut into steps of 32 (zero past k, the step count
+ * rounded up to a multiple of 4).  Per output, with v_mfma_f32_16x16x32 of
+ * the weight type (its result does not depend on the tile position): a hi
+ * chain over the p1 products restarts from +0 every 4 steps and each such
+ * sum is added in f32, in step order, to a running total from +0; one lo
+ * chain from +0 takes the p2 then p3 products of every step; y = total +
+ * lo.  Measured on MI355X: per-output error below 1e-6 relative for
+ * k <= 4096 with N(0,1) activations.  Both routes then need scratch
+ * (eidm_query) for the split activations.
  * An id >= n_experts makes its output row quiet NaN (no weights are read).
  * AUTO runs Grouped when it is legal, scratch covers it and the routed rows
  * average at least 2 per expert (m*top_k >= 2*n_experts); Direct otherwise.
@@ -270,13 +299,15 @@ int eidm_matmul_id(const eidm_shape* shape, int route, const void* weights, uint
 /*
  * eidm_matmul_id for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation):
- * the same computation and bits, with no scratch argument.  The Grouped
- * route's id -> row map lives in a device array the library owns, 8 MiB per
- * GPU, held from the first call on that GPU until the process ends; the call
- * itself allocates nothing.  Arguments as in eidm_matmul_id (weights, input,
- * ids and output are still the caller's).  GROUPED fails with EIDM_E_SIZE,
- * before anything is enqueued, when the map needs more than 8 MiB
- * (eidm_query's scratch_bytes); AUTO then runs Direct.  Every call on one
+ * the same computation and bits, with no scratch argument.  The scratch a
+ * route needs (the Grouped route's id -> row map; with EIDM_ARITH_SPLIT16
+ * the split activations of either route) lives in a device array the
+ * library owns, 8 MiB per GPU, held from the first call on that GPU until
+ * the process ends; the call itself allocates nothing.  Arguments as in
+ * eidm_matmul_id (weights, input, ids and output are still the caller's).
+ * DIRECT or GROUPED fails with EIDM_E_SIZE, before anything is enqueued,
+ * when its scratch (eidm_query's scratch_bytes) exceeds 8 MiB; AUTO then
+ * runs Direct.  Every call on one
  * GPU uses the same array, so calls whose work overlaps in time on one GPU
  * (several streams or host threads) race; issue them on one stream.
  */

@@ -66,7 +66,7 @@ def test_query_auto_picks_direct_for_decode_and_grouped_for_prefill(lib):
     ("m", 0, B.E_INVALID), ("n", 0, B.E_INVALID), ("k", 0, B.E_INVALID),
     ("top_k", 0, B.E_INVALID), ("n_experts", 0, B.E_INVALID),
     ("weight_dtype", 7, B.E_INVALID), ("input_layout", 2, B.E_INVALID),
-    ("id_multiplicity", 5, B.E_INVALID), ("reserved0", 1, B.E_INVALID),
+    ("id_multiplicity", 5, B.E_INVALID), ("arith", 2, B.E_INVALID),
     ("struct_size", 40, B.E_INVALID), ("top_k", 5, B.E_INVALID),  # 5 distinct of 4
     ("expert_stride_bytes", 139, B.E_ALIGN),  # not a multiple of 4
     ("expert_stride_bytes", 136, B.E_INVALID),  # shorter than one expert (140 B)
@@ -372,3 +372,47 @@ def test_calibration_case_limit_fails_closed(lib):
         assert L.eidm_plan_route(plan, ctypes.byref(c), ctypes.byref(route)) == B.E_UNSUPPORTED
     finally:
         L.eidm_plan_destroy(plan)
+
+
+def test_split16_shape_rules_and_scratch(lib):
+    """The split-16 arithmetic: 16-bit weights only, k a multiple of 8; both
+    routes need scratch for the split activations (three 16-bit parts per
+    input element), Grouped the map as well."""
+    s = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2, arith=B.ARITH_SPLIT16)
+    d = lib.query(s, B.DIRECT)
+    g = lib.query(s, B.GROUPED)
+    split = (64 * 256 * 6 + 255) // 256 * 256
+    assert d.scratch_bytes == split
+    s0 = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2)
+    assert lib.query(s0, B.DIRECT).scratch_bytes == 0
+    assert g.scratch_bytes == lib.query(s0, B.GROUPED).scratch_bytes + split
+    slot = B.make_shape(B.F16, 64, 128, 256, 4, 16, 128 * 256 * 2, layout=B.SLOTTED, arith=B.ARITH_SPLIT16)
+    assert lib.query(slot, B.DIRECT).scratch_bytes == (64 * 4 * 256 * 6 + 255) // 256 * 256
+    for bad, code in [(B.make_shape(B.F32, 64, 128, 256, 4, 16, 128 * 256 * 4, arith=B.ARITH_SPLIT16), B.E_UNSUPPORTED),
+                      (B.make_shape(B.BF16, 64, 128, 252, 4, 16, 128 * 252 * 2, arith=B.ARITH_SPLIT16), B.E_UNSUPPORTED),
+                      (B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2, arith=7), B.E_INVALID)]:
+        with pytest.raises(B.EidmError) as e:
+            lib.query(bad, B.DIRECT)
+        assert e.value.code == code
+
+
+def test_split16_rejects_before_launch(lib):
+    L = lib.lib
+    P = ctypes.c_void_p
+    s = B.make_shape(B.BF16, 8, 64, 128, 2, 4, 64 * 128 * 2, arith=B.ARITH_SPLIT16)
+    wb = 4 * 64 * 128 * 2
+    need = lib.query(s, B.DIRECT).scratch_bytes
+    # Direct needs the split scratch too
+    assert L.eidm_matmul_id(ctypes.byref(s), B.DIRECT, P(FAKE), wb, P(FAKE), P(FAKE), P(FAKE), None, 0, None,
+                            None) == B.E_SIZE
+    assert L.eidm_matmul_id(ctypes.byref(s), B.DIRECT, P(FAKE), wb, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                            need - 1, None, None) == B.E_SIZE
+    # 16-byte alignment of weights, stride and input
+    assert L.eidm_matmul_id(ctypes.byref(s), B.DIRECT, P(FAKE + 8), wb, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                            need, None, None) == B.E_ALIGN
+    assert L.eidm_matmul_id(ctypes.byref(s), B.DIRECT, P(FAKE), wb, P(FAKE + 4), P(FAKE), P(FAKE), P(FAKE),
+                            need, None, None) == B.E_ALIGN
+    s2 = B.make_shape(B.BF16, 8, 64, 128, 2, 4, 64 * 128 * 2 + 8, arith=B.ARITH_SPLIT16)
+    assert L.eidm_matmul_id(ctypes.byref(s2), B.DIRECT, P(FAKE), wb + 32, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                            need, None, None) == B.E_ALIGN
+    assert lib.last_dispatch().dispatch_count == 0
