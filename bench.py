@@ -45,6 +45,7 @@ from expert_id_matmul_amd import workloads as W  # noqa: E402
 
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 F32_PEAK = 157.3e12          # flop/s, MI355X dense f32 matrix
+MX16_PEAK = 2.5e15           # flop/s, MI355X dense bf16 / f16 matrix
 ROT = 32                     # decode steps per full sweep of the experts
 PREFILL_STEPS = 16           # matmul calls per timed prefill graph
 
@@ -277,6 +278,20 @@ def bench_prefill(lib, name: str, steps: int, warmup: int):
     # Direct on the same inputs, for the route comparison (not the headline)
     dm = kernel_times(lambda i: matmul(i, B.DIRECT), 3)
     res["direct_tflops"] = flops / (float(np.median(dm)) * 1e-3) / 1e12
+    # the same matmul in the split-16 arithmetic (activation split + map +
+    # Grouped per call); its roofline is the 16-bit matrix peak, on the
+    # algorithmic flops (the three parts per activation are not counted)
+    s16_shape = B.shape_of(wl.with_(arith=B.ARITH_SPLIT16))
+    s16_scratch = torch.empty(lib.query(s16_shape, B.GROUPED).scratch_bytes, dtype=torch.uint8, device="cuda")
+
+    def matmul16(i):
+        lib.matmul_id(s16_shape, B.GROUPED, weights, x, ids, y, s16_scratch, weight_bytes=wl.weight_bytes)
+
+    m16 = Timed(matmul16, 4).run(PREFILL_STEPS, 8, repeats=3)
+    per16 = float(np.median(m16["repeats_gpu_ms_per_step"]))
+    res["split16"] = {"per_call_ms": per16, "repeats": m16["repeats_gpu_ms_per_step"],
+                      "tflops": flops / (per16 * 1e-3) / 1e12}
+    del s16_scratch
     del weights
     torch.cuda.empty_cache()
     return res
@@ -492,7 +507,11 @@ def main():
                        "tflops_matmul": round(v["grouped_tflops"], 2),
                        "frac_f32_peak_matmul": round(v["grouped_tflops"] * 1e12 / F32_PEAK, 4),
                        "ms_per_step": round(v["gpu_ms_per_step"], 4),
-                       "matmul_ms": v["matmul_ms"], "direct_tflops": round(v["direct_tflops"], 2)}
+                       "matmul_ms": v["matmul_ms"], "direct_tflops": round(v["direct_tflops"], 2),
+                       "split16": {"tflops_matmul": round(v["split16"]["tflops"], 2),
+                                   "ms": round(v["split16"]["per_call_ms"], 4),
+                                   "frac_16bit_peak": round(v["split16"]["tflops"] * 1e12 / MX16_PEAK, 4),
+                                   "vs_f32_order": round(v["split16"]["tflops"] / v["grouped_tflops"], 3)}}
                    for k, v in prefill.items()}
     if dec is None:
         print(json.dumps({"prefill": prefill_out}), flush=True)

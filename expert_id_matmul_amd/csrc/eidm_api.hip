@@ -170,12 +170,26 @@ int check_shape(const eidm_shape* s, Plan* p) {
     p->off_counts = align256(eidm::map_hist_elements(routed, s->n_experts) * 4);
     p->off_offsets = p->off_counts + align256((uint64_t)(s->n_experts + 1) * 4);
     p->off_rows = p->off_offsets + align256((uint64_t)(s->n_experts + 2) * 4);
-    p->off_split = p->off_rows + align256(routed * 4);
+    // the row list keeps 32 spare entries: a Grouped kernel reads a job's
+    // 32 entries at once, also for the last bucket
+    p->off_split = p->off_rows + align256((routed + 32) * 4);
     p->grouped_scratch = p->off_split;
     if (s->arith == EIDM_ARITH_SPLIT16) {
-        uint64_t split;  // three 16-bit parts per input element
-        if (!mul_ok(in_el, 6, &split)) return api_fail(EIDM_E_INVALID, "split input size overflows");
-        p->direct_scratch = align256(split);
+        // three 16-bit parts per input element, rows padded to whole 128-k
+        // rounds (16 chunks of 8), plus a 256-byte zero block
+        uint64_t split;
+        const uint64_t row_chunks = ((uint64_t)s->k + 127) / 128 * 16;
+        if (!mul_ok(in_rows, row_chunks, &split) || !mul_ok(split, 48, &split) || !add_ok(split, 256 + 255, &split))
+            return api_fail(EIDM_E_INVALID, "split input size overflows");
+        p->direct_scratch = split & ~uint64_t(255);
+        if (p->direct_scratch < eidm::split16_bytes(in_rows, s->k))
+            return api_fail(EIDM_E_INVALID, "split input size mismatch");
+        // the split-16 kernels address an expert's matrix and the split
+        // activations with 32-bit buffer offsets
+        if (body >= (1ull << 31) || p->direct_scratch >= (1ull << 31))
+            return api_fail(EIDM_E_UNSUPPORTED,
+                            "the split-16 arithmetic needs each expert's matrix and the split activations "
+                            "below 2 GiB");
         if (!add_ok(p->grouped_scratch, p->direct_scratch, &p->grouped_scratch))
             return api_fail(EIDM_E_INVALID, "scratch size overflows");
     }

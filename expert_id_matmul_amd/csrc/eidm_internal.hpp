@@ -84,6 +84,8 @@ bool grouped16_supported(const MatmulArgs& a);
 hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 // The split-16 arithmetic: the activation split (input -> a.xsplit), then
 // the Direct or the Grouped form.
+// bytes of the split activations of in_rows rows of k elements
+uint64_t split16_bytes(uint64_t in_rows, uint32_t k);
 hipError_t launch_split16_x(const MatmulArgs& a, hipStream_t stream);
 hipError_t launch_direct_split16(const MatmulArgs& a, hipStream_t stream);
 hipError_t launch_grouped_split16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);

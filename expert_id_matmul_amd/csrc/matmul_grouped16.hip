@@ -277,17 +277,20 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
     // slice sums in the canonical pairing, and the stores.  The eight output
     // rows' offsets are read from LDS first, so their latency is paid once;
     // each total is formed outside the store's branch.
-    auto finish = [&](const G16Job& j) {
+    // TWO: the job has rows in its second 16-row tile (else that tile's
+    // sums are not formed).
+    auto finish = [&](const G16Job& j, auto twoc) __attribute__((always_inline)) {
+        constexpr int NRT = decltype(twoc)::value ? 2 : 1;
         const int col = (int)j.col0 + wave * kG16WN + l16;
         const bool nan_rows = j.e == a.n_experts;
         const bool col_ok = col < n;
         uint32_t yo[2][4];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) yo[rt][v] = yoff_s[j.slot + 16 * rt + 4 * blk + v];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float u[4];
@@ -435,14 +438,26 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
         // stay in bounds and are never used)
         const LoadState Ln = ci + 1 < my_jobs ? load_state(decode(ci + 1)) : Lc;
         const bool two = cj.rc > 16;
+        // each variant ends with its own finish: no control-flow merge sits
+        // between a job's last round and its stores, so the waits before
+        // the stores follow that variant's own loads in flight
         if (!ODD || s0 == 0) {
-            if (two) job_rounds(IntC2<0>{}, BoolC2<true>{}, Ln);
-            else job_rounds(IntC2<0>{}, BoolC2<false>{}, Ln);
+            if (two) {
+                job_rounds(IntC2<0>{}, BoolC2<true>{}, Ln);
+                finish(cj, BoolC2<true>{});
+            } else {
+                job_rounds(IntC2<0>{}, BoolC2<false>{}, Ln);
+                finish(cj, BoolC2<false>{});
+            }
         } else {
-            if (two) job_rounds(IntC2<1>{}, BoolC2<true>{}, Ln);
-            else job_rounds(IntC2<1>{}, BoolC2<false>{}, Ln);
+            if (two) {
+                job_rounds(IntC2<1>{}, BoolC2<true>{}, Ln);
+                finish(cj, BoolC2<true>{});
+            } else {
+                job_rounds(IntC2<1>{}, BoolC2<false>{}, Ln);
+                finish(cj, BoolC2<false>{});
+            }
         }
-        finish(cj);
         Lc = Ln;
         if (ODD) s0 ^= 1;
     }

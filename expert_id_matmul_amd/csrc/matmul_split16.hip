@@ -15,16 +15,18 @@
 //
 // The order, per output (r, j), over steps of 32 k (zero past k; the step
 // count rounded up to a multiple of 4):
-//   hi: the p1 products of steps 4q .. 4q+3 in one chain from +0;
-//       total = total + hi after every 4 steps (f32 add, total from +0);
+//   hi: one chain from +0 over all steps, the p1 products;
 //   lo: one chain from +0 over all steps, the p2 then the p3 products;
-//   y = total + lo.
+//   y = hi + lo (one f32 add).
 // Operand layout of one instruction (16 x 16 x 32): lane l supplies row or
 // column l % 16 with k elements 8*(l/16) .. 8*(l/16)+7 of the step; result
 // register v of lane l is row 4*(l/16) + v, column l % 16.
 //
 // The activations are split once per call into a scratch buffer: chunk c of
 // 8 consecutive input elements becomes three 16-byte groups (p1, p2, p3).
+// The buffer starts with a block of zeros, and each row is padded with zero
+// chunks to a whole number of 128-k rounds, so no load needs a bounds test
+// on its data: a load past k reads the zero block instead.
 #include <atomic>
 
 #include "eidm_device.hpp"
@@ -38,7 +40,11 @@ typedef _Float16 s16_f16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int s16u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSplitChunkHalves = 24;  // 16-bit elements per split chunk (3 parts x 8)
-constexpr int kStepsPerRound = 4;      // steps of 32 k between hi restarts
+constexpr int kStepsPerRound = 4;      // steps of 32 k per round (128 k)
+constexpr int kZeroHalves = 128;       // the zero block at the start of the split buffer (256 bytes)
+
+// split chunks per row: k/8 rounded up to a whole number of rounds (16 chunks)
+__host__ __device__ inline uint32_t s16_row_chunks(uint32_t k) { return (k + 127) / 128 * 16; }
 
 template <int DT>
 __device__ __forceinline__ f32x4 s16_mfma(const s16u32x4& a, const s16u32x4& b, f32x4 c) {
@@ -82,18 +88,32 @@ __device__ __forceinline__ void s16_split(float v, uint32_t& p1, uint32_t& p2, u
     p3 = s16_round<DT>(r2);
 }
 
+// xs: the zero block, then rows of s16_row_chunks(k) chunks (zero past k)
 template <int DT>
-__global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, uint64_t chunks,
+__global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, uint32_t k, uint64_t rows,
                                                       uint16_t* __restrict__ xs) {
+    const uint32_t kc = k / 8, kcp = s16_row_chunks(k);
+    const uint64_t chunks = rows * kcp;
+    if (blockIdx.x == 0 && threadIdx.x < kZeroHalves / 8)
+        reinterpret_cast<s16u32x4*>(xs)[threadIdx.x] = s16u32x4{0u, 0u, 0u, 0u};
+    uint16_t* body = xs + kZeroHalves;
     for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
          c += (uint64_t)gridDim.x * blockDim.x) {
-        const f32x4 a = reinterpret_cast<const f32x4*>(x)[2 * c];
-        const f32x4 b = reinterpret_cast<const f32x4*>(x)[2 * c + 1];
+        const uint64_t row = c / kcp;
+        const uint32_t ch = (uint32_t)(c - row * kcp);
+        s16u32x4* out = reinterpret_cast<s16u32x4*>(body + c * kSplitChunkHalves);
+        if (ch >= kc) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) out[q] = s16u32x4{0u, 0u, 0u, 0u};
+            continue;
+        }
+        const f32x4* src = reinterpret_cast<const f32x4*>(x + row * k + 8ull * ch);
+        const f32x4 a = src[0];
+        const f32x4 b = src[1];
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t p[3][8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) s16_split<DT>(v[t], p[0][t], p[1][t], p[2][t]);
-        s16u32x4* out = reinterpret_cast<s16u32x4*>(xs + c * kSplitChunkHalves);
 #pragma unroll
         for (int q = 0; q < 3; ++q)
             out[q] = s16u32x4{p[q][0] | (p[q][1] << 16), p[q][2] | (p[q][3] << 16), p[q][4] | (p[q][5] << 16),
@@ -101,15 +121,26 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ 
     }
 }
 
+// A buffer offset past every extent: a buffer load there returns zeros.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t s16_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ s16u32x4 s16_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- Direct
 // One wavefront per (routed row, 32 columns): the row is live in tile row 0
-// (lanes 0, 16, 32, 48 supply its parts; the other rows are zero), two
-// 16-column tiles.  Operands of a round (4 steps) are loaded one round ahead.
+// (lanes 0, 16, 32, 48 supply its parts; the other lanes load zeros), two
+// 16-column tiles.  Operands are loaded two rounds ahead, every round the
+// same loads (past the last round, or past k, they return zeros).
 constexpr int kDs16Cols = 32;
 
 template <int DT>
-__global__ __launch_bounds__(64) void direct_split16_kernel(MatmulArgs a) {
-    const uint32_t n = a.n, k = a.k, kc = a.k / 8;
+__global__ __launch_bounds__(64) void direct_split16_kernel(MatmulArgs a, uint32_t xsplit_bytes) {
+    const uint32_t n = a.n, k = a.k, kc = a.k / 8, kcp = s16_row_chunks(a.k);
     const uint32_t col_tiles = (n + kDs16Cols - 1) / kDs16Cols;
     const uint32_t r = blockIdx.x / col_tiles;
     const uint32_t c0 = (blockIdx.x - r * col_tiles) * kDs16Cols;
@@ -121,46 +152,36 @@ __global__ __launch_bounds__(64) void direct_split16_kernel(MatmulArgs a) {
         return;
     }
     const uint32_t xr = a.layout == 1 ? r : r / a.top_k;
-    const uint16_t* xs = a.xsplit + (size_t)xr * kc * kSplitChunkHalves;
     const bool live = l16 == 0;
-    const uint8_t* wexp = static_cast<const uint8_t*>(a.weights) + (size_t)e * a.stride;
-    const uint8_t* wrow[2];
+    const __amdgpu_buffer_rsrc_t xrs = s16_rsrc(a.xsplit, xsplit_bytes);
+    const uint32_t xbase = kZeroHalves * 2 + xr * kcp * 48 + (uint32_t)g * 48;  // this lane's chunk 0
+    const __amdgpu_buffer_rsrc_t wrs =
+        s16_rsrc(static_cast<const uint8_t*>(a.weights) + (size_t)e * a.stride, n * k * 2);
+    uint32_t woff[2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const uint32_t col = min(c0 + 16 * ct + l16, n - 1);
-        wrow[ct] = wexp + (size_t)col * k * 2;
-    }
+    for (int ct = 0; ct < 2; ++ct) woff[ct] = min(c0 + 16 * ct + l16, n - 1) * k * 2 + (uint32_t)g * 16;
     const uint32_t rounds = (k + 127) / 128;
     struct Ops {
         s16u32x4 x[kStepsPerRound][3];
         s16u32x4 w[kStepsPerRound][2];
     };
     auto load = [&](uint32_t q, Ops& o) {
+        const bool inq = q < rounds;
 #pragma unroll
         for (int s = 0; s < kStepsPerRound; ++s) {
-            const uint32_t ch = 16 * q + 4 * s + g;  // this lane's chunk of the step
-            const bool in = ch < kc;
-            const uint32_t cc = in ? ch : kc - 1;
+            const uint32_t step = 16 * q + 4 * s;  // first chunk of the step
+            const uint32_t xo = live && inq ? xbase + step * 48 : kOob;
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                s16u32x4 v = {0u, 0u, 0u, 0u};
-                if (live) v = *reinterpret_cast<const s16u32x4*>(xs + (size_t)cc * kSplitChunkHalves + 8 * p);
-                o.x[s][p] = in ? v : s16u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int p = 0; p < 3; ++p) o.x[s][p] = s16_load(xrs, xo + 16 * p);
+            const bool wk = inq && step + g < kc;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const s16u32x4 v = *reinterpret_cast<const s16u32x4*>(wrow[ct] + (size_t)cc * 16);
-                o.w[s][ct] = in ? v : s16u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int ct = 0; ct < 2; ++ct) o.w[s][ct] = s16_load(wrs, wk ? woff[ct] + step * 16 : kOob);
         }
     };
-    f32x4 tot[2], lo[2];
+    f32x4 hi[2], lo[2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) tot[ct] = lo[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ct = 0; ct < 2; ++ct) hi[ct] = lo[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     auto compute = [&](const Ops& o) {
-        f32x4 hi[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) hi[ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < kStepsPerRound; ++s)
 #pragma unroll
@@ -169,42 +190,36 @@ __global__ __launch_bounds__(64) void direct_split16_kernel(MatmulArgs a) {
                 lo[ct] = s16_mfma<DT>(o.x[s][1], o.w[s][ct], lo[ct]);
                 lo[ct] = s16_mfma<DT>(o.x[s][2], o.w[s][ct], lo[ct]);
             }
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) tot[ct][v] = tot[ct][v] + hi[ct][v];
     };
     // two register slots with static names, each refilled two rounds ahead
     Ops o0, o1;
     load(0, o0);
-    if (rounds > 1) load(1, o1);
+    load(1, o1);
     for (uint32_t q = 0; q < rounds; q += 2) {
         compute(o0);
-        if (q + 2 < rounds) load(q + 2, o0);
-        if (q + 1 < rounds) {
-            compute(o1);
-            if (q + 3 < rounds) load(q + 3, o1);
-        }
+        load(q + 2, o0);
+        if (q + 1 < rounds) compute(o1);
+        load(q + 3, o1);
     }
     // tile row 0: register 0 of lanes 0..15
     if (g == 0) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const uint32_t col = c0 + 16 * ct + l16;
-            if (col < n) yrow[col] = tot[ct][0] + lo[ct][0];
+            if (col < n) yrow[col] = hi[ct][0] + lo[ct][0];
         }
     }
 }
 
 // ---------------------------------------------------------------- Grouped
-// A job is 32 gathered rows of one expert (two 16-row tiles) by 128 output
-// columns; a block of 4 wavefronts takes 32 columns each (two 16-column
-// tiles).  Per round of 128 k the block stages the split activations of its
-// 32 rows in LDS (double buffer); each wavefront's weights go straight into
-// registers.  The rounds of all the jobs a block walks form one stream, its
-// loads two rounds ahead.
+// A job is 32 gathered rows of one expert (two 16-row tiles) by 64*CT
+// output columns; a block of 4 wavefronts takes 16*CT columns each (CT
+// 16-column tiles; more columns per job read the activation tile fewer
+// times).  Per round of 128 k the block stages the split activations of its
+// 32 rows in LDS; each wavefront's weights go straight into registers.  The
+// rounds of all the jobs a block walks form one stream, its loads two rounds
+// ahead.
 constexpr int kGs16BM = 32;
-constexpr int kGs16BN = 128;
 constexpr int kGs16Waves = 4;
 constexpr int kGs16Threads = 64 * kGs16Waves;
 constexpr int kGs16RowBytes = 16 * 48 + 16;               // one row's 16 chunks of a round, padded
@@ -216,8 +231,8 @@ struct Gs16Job {
     uint32_t e, rc, col0, rbase;
 };
 
-template <int DT>
-__global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(MatmulArgs a,
+template <int DT, int CT>
+__global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(MatmulArgs a, uint32_t xsplit_bytes,
                                                                           const uint32_t* __restrict__ counts,
                                                                           const uint32_t* __restrict__ offsets,
                                                                           const uint32_t* __restrict__ rows) {
@@ -231,8 +246,9 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
-    const uint32_t n = a.n, k = a.k, kc = a.k / 8;
-    const uint32_t ntiles = (n + kGs16BN - 1) / kGs16BN;
+    const uint32_t n = a.n, k = a.k, kc = a.k / 8, kcp = s16_row_chunks(a.k);
+    constexpr uint32_t BN = 64 * CT;
+    const uint32_t ntiles = (n + BN - 1) / BN;
     const uint32_t R = (k + 127) / 128;  // rounds per job
 
     // ---- job table: jobs per bucket -> exclusive prefix
@@ -282,87 +298,96 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
     const uint32_t my_jobs = (job_end - job0 + per_xcd - 1) / per_xcd;
     uint32_t top = 1;
     while (top * 2 <= buckets) top *= 2;
-    auto decode = [&](uint32_t i) {  // block-uniform
+    auto decode = [&](uint32_t i) {  // block-uniform: the fields live in scalar registers
         const uint32_t jb = job0 + i * per_xcd;
         uint32_t e = 0;
         for (uint32_t st = top; st; st >>= 1)
             if (e + st < buckets && job_start[e + st] <= jb) e += st;
-        const uint32_t local = jb - job_start[e];
+        e = __builtin_amdgcn_readfirstlane(e);
+        const uint32_t local = jb - __builtin_amdgcn_readfirstlane(job_start[e]);
         const uint32_t mt = local / ntiles, nt = local - mt * ntiles;
         Gs16Job j;
         j.e = e;
-        j.rc = min((uint32_t)kGs16BM, cnt_s[e] - mt * kGs16BM);
-        j.col0 = nt * kGs16BN;
-        j.rbase = off_s[e] + mt * kGs16BM;
+        j.rc = min((uint32_t)kGs16BM, __builtin_amdgcn_readfirstlane(cnt_s[e]) - mt * kGs16BM);
+        j.col0 = nt * BN;
+        j.rbase = __builtin_amdgcn_readfirstlane(off_s[e]) + mt * kGs16BM;
         return j;
     };
 
-    // ---- load side: the staging role of this thread (row tid/8, chunks
-    // 2*(tid%8) and 2*(tid%8)+1 of a round) and this lane's weight rows
-    const int srow = tid >> 3, schunk = 2 * (tid & 7);
-    struct LoadJob {
-        const uint16_t* xs;     // this thread's staged row, chunk 0
-        const uint8_t* w[2];    // this lane's weight rows (two column tiles)
-    };
-    // the routed row this thread stages for job j (read one job ahead)
-    auto stage_row = [&](const Gs16Job& j) { return rows[j.rbase + ((uint32_t)srow < j.rc ? (uint32_t)srow : 0u)]; };
-    auto load_job = [&](const Gs16Job& j, uint32_t rr) {
-        LoadJob L;
-        const uint32_t xr = a.layout == 1 ? rr : rr / a.top_k;
-        L.xs = a.xsplit + (size_t)xr * kc * kSplitChunkHalves;
-        const uint32_t wexp = j.e < a.n_experts ? j.e : 0u;
-        const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)wexp * a.stride;
+    // ---- load side.  Staging: a round's activation tile is 32 rows x 48
+    // pieces of 16 bytes (16 chunks x 3 parts, contiguous in the split
+    // buffer and in LDS); thread t stages pieces t + 256 j (j < 6), so
+    // consecutive lanes read consecutive pieces of a row.  Rows past the
+    // job's rows read past the buffer (zeros).  Weights: this lane's columns.
+    constexpr int kPieces = kGs16BM * 48 / kGs16Threads;  // 6 per thread
+    const __amdgpu_buffer_rsrc_t xrs = s16_rsrc(a.xsplit, xsplit_bytes);
+    uint32_t prow[kPieces], pm[kPieces], lds_piece[kPieces];
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const uint32_t col = min(j.col0 + 32 * wave + 16 * ct + l16, n - 1);
-            L.w[ct] = base + (size_t)col * k * 2;
+    for (int jj = 0; jj < kPieces; ++jj) {
+        const uint32_t P = (uint32_t)tid + kGs16Threads * jj;
+        prow[jj] = P / 48;
+        pm[jj] = P - prow[jj] * 48;
+        lds_piece[jj] = prow[jj] * kGs16RowBytes + pm[jj] * 16;
+    }
+    struct LoadJob {
+        __amdgpu_buffer_rsrc_t w;    // the expert's matrix
+        uint32_t xoff[kPieces];      // this thread's pieces in round 0 (past the buffer for empty rows)
+        uint32_t woff[CT];           // this lane's weight columns, its chunk of a step
+    };
+    struct StageRows {
+        uint32_t r[kPieces];
+    };
+    // the routed rows of this thread's pieces for job j (read one job ahead)
+    auto stage_row = [&](const Gs16Job& j) {
+        StageRows sr;
+#pragma unroll
+        for (int jj = 0; jj < kPieces; ++jj) sr.r[jj] = rows[j.rbase + (prow[jj] < j.rc ? prow[jj] : 0u)];
+        return sr;
+    };
+    auto load_job = [&](const Gs16Job& j, const StageRows& sr) {
+        LoadJob L;
+#pragma unroll
+        for (int jj = 0; jj < kPieces; ++jj) {
+            const uint32_t xr = a.layout == 1 ? sr.r[jj] : sr.r[jj] / a.top_k;
+            L.xoff[jj] = prow[jj] < j.rc ? kZeroHalves * 2 + xr * kcp * 48 + pm[jj] * 16 : kOob;
         }
+        const uint32_t wexp = j.e < a.n_experts ? j.e : 0u;
+        L.w = s16_rsrc(static_cast<const uint8_t*>(a.weights) + (size_t)wexp * a.stride, n * k * 2);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+            L.woff[ct] = min(j.col0 + 16 * CT * wave + 16 * ct + l16, n - 1) * k * 2 + (uint32_t)g * 16;
         return L;
     };
     struct Stage {
-        s16u32x4 x[2][3];       // two chunks x three parts
-        s16u32x4 w[kStepsPerRound][2];
+        s16u32x4 x[kPieces];    // this thread's staged pieces
+        s16u32x4 w[kStepsPerRound][CT];
     };
-    auto load_round = [&](const LoadJob& L, uint32_t q, Stage& st) {
+    // Every position issues the same loads; past k, and past the end of the
+    // stream, they read at an offset past the buffer and return zeros (the
+    // activation rows are also padded with zero chunks).  With the same
+    // number of loads in flight on every path, each wait before the
+    // matrix-core steps covers exactly the loads it needs.
+    auto load_round = [&](const LoadJob& L, uint32_t q, bool live, Stage& st) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint32_t ch = 16 * q + schunk + c;
-            const bool in = ch < kc;
-            const uint32_t cc = in ? ch : kc - 1;
-#pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                const s16u32x4 v = *reinterpret_cast<const s16u32x4*>(L.xs + (size_t)cc * kSplitChunkHalves + 8 * p);
-                st.x[c][p] = in ? v : s16u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+        for (int jj = 0; jj < kPieces; ++jj) st.x[jj] = s16_load(xrs, live ? L.xoff[jj] + q * 16 * 48 : kOob);
 #pragma unroll
         for (int s = 0; s < kStepsPerRound; ++s) {
-            const uint32_t ch = 16 * q + 4 * s + g;
-            const bool in = ch < kc;
-            const uint32_t cc = in ? ch : kc - 1;
+            const uint32_t step = 16 * q + 4 * s;
+            const bool wk = live && step + g < kc;
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const s16u32x4 v = *reinterpret_cast<const s16u32x4*>(L.w[ct] + (size_t)cc * 16);
-                st.w[s][ct] = in ? v : s16u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int ct = 0; ct < CT; ++ct) st.w[s][ct] = s16_load(L.w, wk ? L.woff[ct] + step * 16 : kOob);
         }
     };
     auto store_x = [&](int buf, const Stage& st) {
-        uint8_t* dst = xbuf + buf * kGs16Buf + srow * kGs16RowBytes + schunk * 48;
+        uint8_t* dst = xbuf + buf * kGs16Buf;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int p = 0; p < 3; ++p) *reinterpret_cast<s16u32x4*>(dst + c * 48 + p * 16) = st.x[c][p];
+        for (int jj = 0; jj < kPieces; ++jj) *reinterpret_cast<s16u32x4*>(dst + lds_piece[jj]) = st.x[jj];
     };
 
-    // ---- compute side
-    f32x4 tot[2][2], lo[2][2];
+    // ---- compute side: per output tile a hi chain (first parts) and a lo
+    // chain (second then third parts), both from +0 over the whole job
+    f32x4 hi[2][CT], lo[2][CT];
     auto compute_round = [&](int buf, const Stage& st) {
-        f32x4 hi[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) hi[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         const uint8_t* src = xbuf + buf * kGs16Buf + l16 * kGs16RowBytes + g * 48;
 #pragma unroll
         for (int s = 0; s < kStepsPerRound; ++s) {
@@ -375,28 +400,29 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
+                for (int ct = 0; ct < CT; ++ct) {
                     hi[rt][ct] = s16_mfma<DT>(xa[rt][0], st.w[s][ct], hi[rt][ct]);
                     lo[rt][ct] = s16_mfma<DT>(xa[rt][1], st.w[s][ct], lo[rt][ct]);
                     lo[rt][ct] = s16_mfma<DT>(xa[rt][2], st.w[s][ct], lo[rt][ct]);
                 }
         }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) tot[rt][ct][v] = tot[rt][ct][v] + hi[rt][ct][v];
     };
-    // the output rows of this lane's results (read when the job starts)
+    // The output rows of this lane's results, read when the job starts.
+    // The job's 32 row-list entries are read with block-uniform (scalar)
+    // loads, whose wait does not hold up the vector loads in flight; the
+    // row list has 32 spare entries past its end, so the read stays in
+    // bounds for the last bucket (entries past the job's rows are not used).
     uint32_t yrows[2][4];
     auto read_yrows = [&](const Gs16Job& j) {
+        uint32_t ent[kGs16BM];
+#pragma unroll
+        for (int i = 0; i < kGs16BM; ++i) ent[i] = __builtin_amdgcn_readfirstlane(rows[j.rbase + i]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const uint32_t i = 16 * rt + 4 * g + v;
-                yrows[rt][v] = rows[j.rbase + (i < j.rc ? i : 0u)];
+                const int i = 16 * rt + v;
+                yrows[rt][v] = g == 0 ? ent[i] : g == 1 ? ent[i + 4] : g == 2 ? ent[i + 8] : ent[i + 12];
             }
     };
     auto finish = [&](const Gs16Job& j) {
@@ -409,15 +435,15 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
                 if (i >= j.rc) continue;
                 float* yrow = a.output + (size_t)yrows[rt][v] * n;
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    const uint32_t col = j.col0 + 32 * wave + 16 * ct + l16;
-                    if (col < n) yrow[col] = nan_rows ? quiet_nan() : tot[rt][ct][v] + lo[rt][ct][v];
+                for (int ct = 0; ct < CT; ++ct) {
+                    const uint32_t col = j.col0 + 16 * CT * wave + 16 * ct + l16;
+                    if (col < n) yrow[col] = nan_rows ? quiet_nan() : hi[rt][ct][v] + lo[rt][ct][v];
                 }
             }
     };
 
     // The stream: position i = (job i / R, round i % R).  Position i is
-    // computed from LDS buffer i % 3 and weight slot i % 3; its loads were
+    // computed from LDS buffer i % 3 and register slot i % 3; its loads were
     // issued at position i - 2 and its activations stored to LDS at
     // position i - 1 (before that position's barrier).
     const uint32_t total_pos = my_jobs * R;
@@ -425,7 +451,7 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
     read_yrows(jc);
     LoadJob Lj = load_job(jc, stage_row(jc));  // job being loaded
     uint32_t lj = 0, lq = 0;            // its job index and round
-    uint32_t next_rr = my_jobs > 1 ? stage_row(decode(1)) : 0u;  // staged row of job lj + 1
+    StageRows next_rr = stage_row(decode(my_jobs > 1 ? 1u : 0u));  // staged rows of job lj + 1
     auto advance_load = [&]() {
         if (++lq == R) {
             lq = 0;
@@ -436,28 +462,25 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
         }
     };
     Stage ring0, ring1, ring2;  // register slots of positions i % 3 (static names: no indexed registers)
-    load_round(Lj, lq, ring0);
+    load_round(Lj, lq, true, ring0);
     advance_load();
-    if (total_pos > 1) {
-        load_round(Lj, lq, ring1);
-        advance_load();
-    }
+    load_round(Lj, lq, total_pos > 1, ring1);
+    if (total_pos > 1) advance_load();
     store_x(0, ring0);
     __syncthreads();
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) tot[rt][ct] = lo[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ct = 0; ct < CT; ++ct) hi[rt][ct] = lo[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t q = 0;  // round of the computed job
     uint32_t ci = 0;
-    // Position i: compute from LDS buffer and register slot i % 3; load
-    // position i + 2 into slot (i + 2) % 3; store position i + 1's staged
+    // Position i: load position i + 2 into slot (i + 2) % 3; compute from
+    // LDS buffer and register slot i % 3; store position i + 1's staged
     // activations into LDS buffer (i + 1) % 3; one barrier.
     auto position = [&](uint32_t i, int buf, Stage& cur, Stage& nxt, Stage& ahead) __attribute__((always_inline)) {
-        if (i + 2 < total_pos) {
-            load_round(Lj, lq, ahead);
-            advance_load();
-        }
+        const bool live = i + 2 < total_pos;
+        load_round(Lj, lq, live, ahead);
+        if (live) advance_load();
         compute_round(buf, cur);
         if (i + 1 < total_pos) store_x(buf == 2 ? 0 : buf + 1, nxt);
         if (++q == R) {
@@ -465,7 +488,7 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) tot[rt][ct] = lo[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int ct = 0; ct < CT; ++ct) hi[rt][ct] = lo[rt][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             q = 0;
             if (++ci < my_jobs) {
                 jc = decode(ci);
@@ -483,52 +506,88 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
 
 }  // namespace
 
+uint64_t split16_bytes(uint64_t in_rows, uint32_t k) {
+    return (uint64_t)kZeroHalves * 2 + in_rows * s16_row_chunks(k) * kSplitChunkHalves * 2;
+}
+
 hipError_t launch_split16_x(const MatmulArgs& a, hipStream_t stream) {
     const uint64_t in_rows = a.layout == 1 ? (uint64_t)a.m * a.top_k : a.m;
-    const uint64_t chunks = in_rows * (a.k / 8);
+    const uint64_t chunks = in_rows * s16_row_chunks(a.k);
     uint64_t blocks = (chunks + 255) / 256;
     if (blocks > 16384) blocks = 16384;
     if (blocks == 0) blocks = 1;
     if (a.dtype == kDtypeF16)
-        hipLaunchKernelGGL(split_x_kernel<kDtypeF16>, dim3((uint32_t)blocks), dim3(256), 0, stream, a.input, chunks,
-                           a.xsplit);
+        hipLaunchKernelGGL(split_x_kernel<kDtypeF16>, dim3((uint32_t)blocks), dim3(256), 0, stream, a.input, a.k,
+                           in_rows, a.xsplit);
     else
-        hipLaunchKernelGGL(split_x_kernel<kDtypeBF16>, dim3((uint32_t)blocks), dim3(256), 0, stream, a.input, chunks,
-                           a.xsplit);
+        hipLaunchKernelGGL(split_x_kernel<kDtypeBF16>, dim3((uint32_t)blocks), dim3(256), 0, stream, a.input, a.k,
+                           in_rows, a.xsplit);
     return launched(EIDM_KERNEL_SPLIT_X, (uint32_t)blocks, 256, 0);
+}
+
+// buffer loads take 32-bit offsets: each expert's matrix and the split
+// activations must span less than 2 GiB (checked when the shape is
+// validated)
+static uint32_t split_bytes_of(const MatmulArgs& a) {
+    const uint64_t in_rows = a.layout == 1 ? (uint64_t)a.m * a.top_k : a.m;
+    return (uint32_t)split16_bytes(in_rows, a.k);
 }
 
 hipError_t launch_direct_split16(const MatmulArgs& a, hipStream_t stream) {
     const uint64_t routed = (uint64_t)a.m * a.top_k;
     const uint64_t blocks = routed * ((a.n + kDs16Cols - 1) / kDs16Cols);
     if (blocks > 0x7fffffffull) return hipErrorInvalidValue;
+    const uint32_t xb = split_bytes_of(a);
     if (a.dtype == kDtypeF16)
-        hipLaunchKernelGGL(direct_split16_kernel<kDtypeF16>, dim3((uint32_t)blocks), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(direct_split16_kernel<kDtypeF16>, dim3((uint32_t)blocks), dim3(64), 0, stream, a, xb);
     else
-        hipLaunchKernelGGL(direct_split16_kernel<kDtypeBF16>, dim3((uint32_t)blocks), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(direct_split16_kernel<kDtypeBF16>, dim3((uint32_t)blocks), dim3(64), 0, stream, a, xb);
     return launched(EIDM_KERNEL_DIRECT_SPLIT16, (uint32_t)blocks, 64, 0);
 }
 
-hipError_t launch_grouped_split16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream) {
+template <int DT, int CT>
+hipError_t launch_gs16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream) {
     const uint64_t routed = (uint64_t)a.m * a.top_k;
-    const uint64_t ntiles = (a.n + kGs16BN - 1) / kGs16BN;
+    const uint64_t ntiles = (a.n + 64 * CT - 1) / (64 * CT);
     const uint64_t job_bound = (routed / kGs16BM + a.n_experts + 1) * ntiles;
     const size_t lds = (size_t)kGs16Bufs * kGs16Buf + (3 * (size_t)a.n_experts + 4) * sizeof(uint32_t);
-    auto kernel = a.dtype == kDtypeF16 ? grouped_split16_kernel<kDtypeF16> : grouped_split16_kernel<kDtypeBF16>;
-    static std::atomic<uint32_t> raised{0};
-    const uint32_t bit = a.dtype == kDtypeF16 ? 1u : 2u;
-    if (!(raised.load(std::memory_order_relaxed) & bit)) {
+    auto kernel = grouped_split16_kernel<DT, CT>;
+    static std::atomic<bool> raised{false};
+    if (!raised.load(std::memory_order_relaxed)) {
         const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (err != hipSuccess) return err;
-        raised.fetch_or(bit, std::memory_order_relaxed);
+        raised.store(true, std::memory_order_relaxed);
     }
     const uint64_t resident = (uint64_t)(device_cus > 0 ? device_cus : 256);
     uint64_t grid = job_bound < resident ? job_bound : resident;
     grid = (grid + kGs16Xcds - 1) / kGs16Xcds * kGs16Xcds;
-    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kGs16Threads), lds, stream, a, buf.counts, buf.offsets,
-                       buf.rows);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kGs16Threads), lds, stream, a, split_bytes_of(a), buf.counts,
+                       buf.offsets, buf.rows);
     return launched(EIDM_KERNEL_GROUPED_SPLIT16, (uint32_t)grid, kGs16Threads, (uint32_t)lds);
+}
+
+// Columns per wavefront: 3 16-column tiles when that job count (estimated
+// from the routed rows, as whole 32-row tiles) gives the busiest compute
+// unit no more work than 2 tiles would, else 2.  (4 tiles spill registers
+// and measured slower.)
+int gs16_column_tiles(const MatmulArgs& a, int device_cus) {
+    const uint64_t row_tiles = ((uint64_t)a.m * a.top_k + kGs16BM - 1) / kGs16BM;
+    const uint64_t cus = (uint64_t)(device_cus > 0 ? device_cus : 256);
+    auto makespan = [&](uint64_t ct) {
+        const uint64_t jobs = row_tiles * ((a.n + 64 * ct - 1) / (64 * ct));
+        return (jobs + cus - 1) / cus * ct;  // jobs of the busiest unit x columns per job
+    };
+    return makespan(3) <= makespan(2) ? 3 : 2;
+}
+
+hipError_t launch_grouped_split16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream) {
+    const int ct = gs16_column_tiles(a, device_cus);
+    if (a.dtype == kDtypeF16)
+        return ct == 3 ? launch_gs16<kDtypeF16, 3>(a, buf, device_cus, stream)
+                       : launch_gs16<kDtypeF16, 2>(a, buf, device_cus, stream);
+    return ct == 3 ? launch_gs16<kDtypeBF16, 3>(a, buf, device_cus, stream)
+                   : launch_gs16<kDtypeBF16, 2>(a, buf, device_cus, stream);
 }
 
 }  // namespace eidm

@@ -282,12 +282,12 @@ uint64_t eidm_map_scratch_bytes(uint32_t m, uint32_t top_k, uint32_t n_experts);
  * 2^-24 round), and k is cut into steps of 32 (zero past k, the step count
  * rounded up to a multiple of 4).  Per output, with v_mfma_f32_16x16x32 of
  * the weight type (its result does not depend on the tile position): a hi
- * chain over the p1 products restarts from +0 every 4 steps and each such
- * sum is added in f32, in step order, to a running total from +0; one lo
- * chain from +0 takes the p2 then p3 products of every step; y = total +
- * lo.  Measured on MI355X: per-output error below 1e-6 relative for
- * k <= 4096 with N(0,1) activations.  Both routes then need scratch
- * (eidm_query) for the split activations.
+ * chain from +0 over the p1 products of every step, a lo chain from +0 over
+ * the p2 then p3 products of every step, y = hi + lo (one f32 add).
+ * Measured on MI355X: per-output error below 3e-6 relative for k <= 4096
+ * with N(0,1) activations.  Each expert's matrix and the split activations
+ * must span less than 2 GiB.  Both routes then need scratch (eidm_query)
+ * for the split activations.
  * An id >= n_experts makes its output row quiet NaN (no weights are read).
  * AUTO runs Grouped when it is legal, scratch covers it and the routed rows
  * average at least 2 per expert (m*top_k >= 2*n_experts); Direct otherwise.

@@ -381,13 +381,16 @@ def test_split16_shape_rules_and_scratch(lib):
     s = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2, arith=B.ARITH_SPLIT16)
     d = lib.query(s, B.DIRECT)
     g = lib.query(s, B.GROUPED)
-    split = (64 * 256 * 6 + 255) // 256 * 256
+    # three 16-bit parts per element, rows padded to whole 128-k rounds, a 256-byte zero block
+    split = (256 + 64 * 2 * 16 * 48 + 255) // 256 * 256
     assert d.scratch_bytes == split
     s0 = B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2)
     assert lib.query(s0, B.DIRECT).scratch_bytes == 0
     assert g.scratch_bytes == lib.query(s0, B.GROUPED).scratch_bytes + split
     slot = B.make_shape(B.F16, 64, 128, 256, 4, 16, 128 * 256 * 2, layout=B.SLOTTED, arith=B.ARITH_SPLIT16)
-    assert lib.query(slot, B.DIRECT).scratch_bytes == (64 * 4 * 256 * 6 + 255) // 256 * 256
+    assert lib.query(slot, B.DIRECT).scratch_bytes == (256 + 64 * 4 * 2 * 16 * 48 + 255) // 256 * 256
+    ragged = B.make_shape(B.BF16, 3, 128, 264, 4, 16, 128 * 264 * 2, arith=B.ARITH_SPLIT16)
+    assert lib.query(ragged, B.DIRECT).scratch_bytes == (256 + 3 * 3 * 16 * 48 + 255) // 256 * 256
     for bad, code in [(B.make_shape(B.F32, 64, 128, 256, 4, 16, 128 * 256 * 4, arith=B.ARITH_SPLIT16), B.E_UNSUPPORTED),
                       (B.make_shape(B.BF16, 64, 128, 252, 4, 16, 128 * 252 * 2, arith=B.ARITH_SPLIT16), B.E_UNSUPPORTED),
                       (B.make_shape(B.BF16, 64, 128, 256, 4, 16, 128 * 256 * 2, arith=7), B.E_INVALID)]:
