@@ -68,26 +68,40 @@ def _canonical_lib():
         so = os.path.join(HERE, "_canonical_f32.so")
         if not os.path.exists(so) or os.path.getmtime(so) < os.path.getmtime(src):
             subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-                            "-fno-fast-math", src, "-o", so + ".tmp", "-lm"], check=True)
+                            "-fno-fast-math", "-pthread", src, "-o", so + ".tmp", "-lm"], check=True)
             os.replace(so + ".tmp", so)
         lib = ctypes.CDLL(so)
         P = ctypes.c_void_p
         u32 = ctypes.c_uint32
         lib.canonical_matmul_id.argtypes = [ctypes.c_int, u32, u32, u32, u32, u32, ctypes.c_uint64,
                                             ctypes.c_int, P, P, P, P]
+        lib.canonical_matmul_id_threads.argtypes = [ctypes.c_int, u32, u32, u32, u32, u32, ctypes.c_uint64,
+                                                    ctypes.c_int, P, P, P, P, ctypes.c_int]
         _canon = lib
     return _canon
 
 
-def canonical_matmul_id(wl, wbytes: np.ndarray, x: np.ndarray, ids: np.ndarray) -> np.ndarray:
+def host_threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
+
+
+def canonical_matmul_id(wl, wbytes: np.ndarray, x: np.ndarray, ids: np.ndarray, threads: int = 1) -> np.ndarray:
     lib = _canonical_lib()
     wb = np.ascontiguousarray(wbytes, dtype=np.uint8)
     x = np.ascontiguousarray(x, dtype=np.float32)
     ids = np.ascontiguousarray(ids, dtype=np.uint32)
     y = np.empty((wl.m * wl.top_k, wl.n), dtype=np.float32)
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
-    lib.canonical_matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride,
-                            wl.layout, p(wb), p(x), p(ids), p(y))
+    if threads > 1:
+        rc = lib.canonical_matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride,
+                                             wl.layout, p(wb), p(x), p(ids), p(y), threads)
+        assert rc == 0, "canonical evaluation: out of host memory"
+    else:
+        lib.canonical_matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride,
+                                wl.layout, p(wb), p(x), p(ids), p(y))
     return y
 
 

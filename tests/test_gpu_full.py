@@ -197,3 +197,41 @@ def test_graph_replays_match_eager(lib):
             assert torch.equal(bufs[k], eager[k]), f"replay {rep}: {k} differs"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def _full_ids_host(wl):
+    if wl.ids_kind == "logits":
+        ids, _, _, _ = oracle.route(W.router_logits(wl), W.router_bias(wl), wl.top_k)
+        return ids
+    return W.ids(wl)
+
+
+@pytest.mark.parametrize("name", ["prefill_balanced", "prefill_skewed", "down_proj"])
+def test_full_size_whole_output_equals_the_documented_order(lib, name):
+    """Every output of the benchmark's Grouped call equals the CPU evaluation
+    of the documented f32 order bit for bit (threaded over the host's cores),
+    and for the balanced configuration every output is also within the bar
+    of the oracle."""
+    from helpers import canonical_matmul_id, host_threads
+    wl = W.WORKLOADS[name]
+    print(f"[case] whole output {name}", flush=True)
+    wdev = _device_weights(wl)
+    xh = W.activations(wl)
+    ih = _full_ids_host(wl)
+    y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
+    taken = lib.matmul_id(B.shape_of(wl), B.GROUPED, wdev, to_dev(xh), ids_to_dev(ih), y, _scratch(lib, wl),
+                          weight_bytes=wl.weight_bytes)
+    torch.cuda.synchronize()
+    assert taken == B.GROUPED
+    yg = y.cpu().numpy()
+    wb = wdev.cpu().numpy()
+    del wdev, y
+    threads = host_threads()
+    ref = canonical_matmul_id(wl, wb, xh, ih, threads=threads)
+    diff = np.flatnonzero(yg.view(np.uint32) != ref.view(np.uint32))
+    assert diff.size == 0, f"{diff.size} outputs differ from the documented order, first at {diff[:5]}"
+    if name == "prefill_balanced":
+        full = oracle.matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout, wb,
+                                        xh, ih, threads)
+        err = assert_close(yg, full, what=f"{name} every output")
+        print(f"[case] {name}: every output vs the oracle, max rel err {err:.3e}", flush=True)

@@ -531,3 +531,31 @@ def test_random_shapes_fused_step_matches_the_three_calls(lib, seed):
           f"layout={layout} bias={with_bias} renorm={renorm}", flush=True)
     _fused_vs_three_calls(lib, _wl(f"rfused{seed}", dtype, m, n, k, top_k, n_experts, layout=layout,
                                    seed=600 + seed), with_bias=with_bias, renormalize=renorm)
+
+
+def test_router_sigmoid_bits_over_ten_million_logits(lib):
+    """gate = sigma(logit) when one expert is picked without renormalising: the
+    GPU's f32 sigma equals the oracle's bit for bit over 10^7 logits spanning
+    [-88, 88] (a uniform grid, random values, and dense runs where sigma
+    saturates to 1 in f32 and where it falls into the subnormal range)."""
+    rng = np.random.default_rng(97)
+    parts = [np.linspace(-88.0, 88.0, 6_000_000, dtype=np.float64).astype(np.float32),
+             rng.uniform(-88.0, 88.0, 2_000_000).astype(np.float32),
+             rng.uniform(15.0, 18.5, 800_000).astype(np.float32),     # sigma -> 1 - 2^-24 .. 1
+             rng.uniform(-88.0, -80.0, 800_000).astype(np.float32),   # sigma below 2^-115, subnormal f32 tail
+             rng.uniform(-1e-3, 1e-3, 399_992).astype(np.float32),
+             np.array([0.0, -0.0, 88.0, -88.0, 1e-30, -1e-30, 17.328680, -87.33655], dtype=np.float32)]
+    logits = np.concatenate(parts).reshape(-1, 1)
+    m = logits.shape[0]
+    assert m >= 10_000_000
+    print(f"[case] sigmoid sweep m={m}", flush=True)
+    ids = torch.empty((m, 1), dtype=torch.int32, device="cuda")
+    gates = torch.empty((m, 1), dtype=torch.float32, device="cuda")
+    lib.route_topk(to_dev(logits), None, 1, ids, gates, renormalize=False)
+    torch.cuda.synchronize()
+    assert (ids.cpu().numpy() == 0).all()
+    _, _, sigma, _ = oracle.route(logits, None, 1, renormalize=False)
+    g = gates.cpu().numpy().view(np.uint32).reshape(-1)
+    o = sigma.view(np.uint32).reshape(-1)
+    bad = np.flatnonzero(g != o)
+    assert bad.size == 0, f"{bad.size} sigma values differ, e.g. logit {logits.reshape(-1)[bad[:3]]}"
