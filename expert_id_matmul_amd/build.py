@@ -15,10 +15,11 @@ LIB = os.path.join(PKG, "libeidm.so")
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["eidm_api.hip", "route.hip", "map.hip", "matmul_direct.hip", "matmul_grouped.hip",
            "matmul_grouped16.hip", "combine.hip", "moe_direct.hip", "validate.hip", "calibrate.hip",
-           "ffn.hip", "noalloc.hip", "matmul_split16.hip"]
-# per-source extra flags: the 16x16x1 Grouped kernel keeps its matrix-core
-# accumulators in the architectural registers (the slice sums are then read
-# by ordinary adds, with no accumulator-register moves)
+           "ffn.hip", "noalloc.hip", "matmul_split16.hip", "matmul_grouped16_acc.hip"]
+# per-source extra flags: the long-job build of the 16x16x1 Grouped kernel
+# keeps its matrix-core accumulators in the architectural registers (the
+# slice sums are then read by ordinary adds, with no accumulator-register
+# moves); matmul_grouped16_acc.hip, the short-job build, keeps the default
 EXTRA = {"matmul_grouped16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -82,6 +82,10 @@ hipError_t launch_grouped(const MatmulArgs& a, const MapBuffers& buf, int device
 // grouped16_supported says so.
 bool grouped16_supported(const MatmulArgs& a);
 hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
+// jobs of at most this many rounds of k run the build of the same kernel
+// that keeps its accumulators in the accumulation registers
+constexpr uint32_t kG16AccRounds = 8;
+hipError_t launch_grouped16_acc(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 // The split-16 arithmetic: the activation split (input -> a.xsplit), then
 // the Direct or the Grouped form.
 // bytes of the split activations of in_rows rows of k elements

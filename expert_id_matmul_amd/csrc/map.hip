@@ -169,12 +169,18 @@ __global__ __launch_bounds__(64 * kMapKeyedWaves) void map_keyed_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t first = (uint32_t)wave * span + (uint32_t)lane;
     const int chunks = (int)(span >> 6);
-    // every id of this wavefront's rows first, then the two counts
-    uint32_t key[kMapKeyedChunks];
+    // every id of this wavefront's rows first, then the two counts.  The
+    // loads are unconditional (rows past the end re-read the last id, and
+    // routed_rows >= 1: zero dimensions are rejected on the host), so all
+    // of them are in flight together; a load under a branch would be waited
+    // for before the next one is issued.
+    uint32_t raw[kMapKeyedChunks], key[kMapKeyedChunks];
+#pragma unroll
+    for (int c = 0; c < kMapKeyedChunks; ++c) raw[c] = ids[min(first + 64u * (uint32_t)c, routed_rows - 1)];
 #pragma unroll
     for (int c = 0; c < kMapKeyedChunks; ++c) {
         const uint32_t r = first + 64u * (uint32_t)c;
-        key[c] = c < chunks && r < routed_rows ? key_of(ids[r], n_experts) : 0xffffffffu;
+        key[c] = c < chunks && r < routed_rows ? key_of(raw[c], n_experts) : 0xffffffffu;
     }
     uint32_t lt = 0, eq = 0;
 #pragma unroll
