@@ -115,12 +115,18 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
     const int R = (k + kRoundK - 1) / kRoundK;  // rounds per job (at least 3)
     const int tail = k - (R - 1) * kRoundK;     // elements of the last round inside k
 
-    // ---- job table: jobs per bucket -> exclusive prefix, with counts and offsets
+    // ---- job table: jobs per bucket -> exclusive prefix, with counts and
+    // offsets.  A job's cost is its number of 16-row tiles (the matrix-core
+    // work: a job of at most 16 rows skips its second tile), so bucket e
+    // costs ceil(count/16) x ntiles.  The job list is cut into one share per
+    // XCD of equal cost: share x starts at the first job whose cost prefix
+    // reaches x/8 of the total.
+    __shared__ uint32_t cost_tot[kG16Waves], share_s[kG16Xcds + 1];
     {
         const uint32_t per = (buckets + kG16Threads - 1) / kG16Threads;
         const uint32_t begin = min(buckets, (uint32_t)tid * per);
         const uint32_t end = min(buckets, begin + per);
-        uint32_t s = 0;
+        uint32_t s = 0, cs = 0;
         for (uint32_t i = begin; i < end; ++i) {
             const uint32_t c = counts[i];
             cnt_s[i] = c;
@@ -128,37 +134,68 @@ __global__ __launch_bounds__(kG16Threads, 1) void grouped16_kernel(MatmulArgs a,
             const uint32_t jobs = ((c + kG16BM - 1) / kG16BM) * ntiles;
             job_start[i] = jobs;
             s += jobs;
+            cs += ((c + 15) / 16) * ntiles;
         }
-        uint32_t inc = s;
+        uint32_t inc = s, cinc = cs;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(inc, d);
-            if (lane >= d) inc += o;
+            const uint32_t o = __shfl_up(inc, d), co = __shfl_up(cinc, d);
+            if (lane >= d) {
+                inc += o;
+                cinc += co;
+            }
         }
-        if (lane == 63) wave_tot[wave] = inc;
+        if (lane == 63) {
+            wave_tot[wave] = inc;
+            cost_tot[wave] = cinc;
+        }
         __syncthreads();
-        uint32_t run = inc - s, total = 0;
+        uint32_t run = inc - s, total = 0, crun = cinc - cs, ctotal = 0;
         for (int w = 0; w < kG16Waves; ++w) {
-            if (w < wave) run += wave_tot[w];
+            if (w < wave) {
+                run += wave_tot[w];
+                crun += cost_tot[w];
+            }
             total += wave_tot[w];
+            ctotal += cost_tot[w];
         }
         for (uint32_t i = begin; i < end; ++i) {
             const uint32_t v = job_start[i];
             job_start[i] = run;
+            // the XCD cuts that fall in this bucket's cost span [crun, crun + cost)
+            const uint32_t c = cnt_s[i];
+            const uint32_t cost = ((c + 15) / 16) * ntiles;
+            for (uint32_t x = 1; x < (uint32_t)kG16Xcds; ++x) {
+                const uint32_t th = (uint32_t)((uint64_t)x * ctotal / kG16Xcds);
+                if (th < crun || th >= crun + cost) continue;
+                // job l of the bucket starts at cost 2l up to its last row tile,
+                // whose jobs cost 1 or 2 each
+                const uint32_t d = th - crun;
+                const uint32_t full2 = 2u * (c / kG16BM) * ntiles;
+                const uint32_t wl = c % kG16BM > 16 ? 2u : 1u;
+                const uint32_t l = d <= full2 ? (d + 1) / 2 : full2 / 2 + (d - full2 + wl - 1) / wl;
+                share_s[x] = run + l;
+            }
             run += v;
+            crun += cost;
         }
-        if (tid == 0) job_start[buckets] = total;
+        if (tid == 0) {
+            job_start[buckets] = total;
+            share_s[0] = 0;
+            share_s[kG16Xcds] = total;
+            if (ctotal == 0)
+                for (int x = 1; x < kG16Xcds; ++x) share_s[x] = total;
+        }
         __syncthreads();
     }
     const uint32_t total_jobs = job_start[buckets];
-    // Each XCD walks one contiguous share of the job list with its blocks side
-    // by side (the hardware deals blocks to the XCDs round-robin), so the
-    // column tiles of one expert's row tile meet in one L2.
+    // Each XCD walks its share of the job list with its blocks side by side
+    // (the hardware deals blocks to the XCDs round-robin), so the column
+    // tiles of one expert's row tile meet in one L2.
     const uint32_t per_xcd = gridDim.x / kG16Xcds;
-    const uint32_t xcd_jobs = (total_jobs + kG16Xcds - 1) / kG16Xcds;
     const uint32_t xcd = blockIdx.x % kG16Xcds;
-    const uint32_t job0 = xcd * xcd_jobs + blockIdx.x / kG16Xcds;
-    const uint32_t job_end = min(total_jobs, (xcd + 1) * xcd_jobs);
+    const uint32_t job0 = share_s[xcd] + blockIdx.x / kG16Xcds;
+    const uint32_t job_end = min(total_jobs, share_s[xcd + 1]);
     if (job0 >= job_end) return;  // the whole block leaves together
     const uint32_t my_jobs = (job_end - job0 + per_xcd - 1) / per_xcd;
 
