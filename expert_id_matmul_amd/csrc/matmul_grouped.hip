@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_kernel(MatmulArgs a,
 // around the load) and replaced by zeros where they are used: activations
 // when stored to LDS, weights in the step that computes the job's last
 // round (known at each call site).
-template <int DT, int R, int C, int WAVES, bool W32, bool ODD, bool TAIL>
+template <int DT, int R, int C, int WAVES, bool ODD, bool TAIL>
 __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a,
                                                                        const uint32_t* __restrict__ counts,
                                                                        const uint32_t* __restrict__ offsets,
@@ -658,35 +658,28 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     };
     // piece i of this lane's granule lies past k in the last round (TAIL)
     auto w_past = [&](int i) { return b * kGranule + i * (16 / S) >= tail; };
-    // this lane's weight granules of round g (columns past n read column n-1)
-    // With W32 (an expert's matrix spans under 4 GB) a load's address is a
-    // block-uniform base (expert and round, in scalar registers) plus a
-    // 32-bit lane offset fixed for the job, so the steady loop spends no
-    // vector instructions on 64-bit addresses.
+    // this lane's weight granules of round g (columns past n read column n-1).
+    // A load's address is a wavefront-uniform base (expert, the column group's
+    // first column and the round, in scalar registers) plus a 32-bit lane
+    // offset below 4*k*S + 1024 (the launch keeps that under 4 GB), so the
+    // steady loop spends no vector instructions on 64-bit addresses, whatever
+    // the size of an expert's matrix.
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto fetch_w = [&](const Job& j, int g, WeightRound<DT, C>& wr) {
         const uint8_t* base = static_cast<const uint8_t*>(a.weights) + (size_t)j.wexp * a.stride;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int col = min((int)j.col0 + wave * 4 * C + 4 * c + q, n - 1);
-            if constexpr (W32) {
-                const uint8_t* rb = base + (size_t)g * kRoundK * S;
-                const uint32_t off = (uint32_t)col * (uint32_t)a.k * (uint32_t)S + (uint32_t)(b * kGranule * S);
+            const int c0 = min((int)j.col0 + wave_u * 4 * C + 4 * c, n - 1);  // uniform
+            const int col = min((int)j.col0 + wave_u * 4 * C + 4 * c + q, n - 1);
+            // the base sits one round back, so a TAIL piece loaded from the
+            // previous round (zeroed in step2) keeps a non-negative offset
+            const uint8_t* rb = base + (size_t)c0 * a.k * S + (size_t)(g - 1) * kRoundK * S;
+            const uint32_t off = (uint32_t)(col - c0) * (uint32_t)a.k * (uint32_t)S + (uint32_t)(b * kGranule * S);
 #pragma unroll
-                for (int i = 0; i < Pieces<DT>::value; ++i) {
-                    const uint8_t* src = rb + off + 16u * (uint32_t)i;
-                    if constexpr (TAIL) src -= g == last && w_past(i) ? kRoundK * S : 0;  // zeroed in step2
-                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(src);
-                }
-            } else if constexpr (TAIL) {
-                const uint8_t* row = base + (size_t)col * a.k * S;
-#pragma unroll
-                for (int i = 0; i < Pieces<DT>::value; ++i) {
-                    int e = g * kRoundK + b * kGranule + i * (16 / S);
-                    e -= g == last && w_past(i) ? kRoundK : 0;  // zeroed in step2
-                    wr.p[c][i] = *reinterpret_cast<const u32x4*>(row + (size_t)e * S);
-                }
-            } else {
-                load_w_pieces<DT>(base + (size_t)col * a.k * S, g * kRoundK + b * kGranule, wr.p[c]);
+            for (int i = 0; i < Pieces<DT>::value; ++i) {
+                const bool back = TAIL && g == last && w_past(i);
+                const uint32_t o = off + 16u * (uint32_t)i + (back ? 0u : (uint32_t)(kRoundK * S));
+                wr.p[c][i] = *reinterpret_cast<const u32x4*>(rb + o);
             }
         }
     };
@@ -878,12 +871,6 @@ __global__ __launch_bounds__(64 * WAVES) void grouped_stream_kernel(MatmulArgs a
     if (i < my_jobs) run_job(IntC<0>{});
 }
 
-template <int DT, int R, int C, int WAVES, bool ODD, bool TAIL>
-auto stream_kernel(bool w32) {
-    return w32 ? grouped_stream_kernel<DT, R, C, WAVES, true, ODD, TAIL>
-               : grouped_stream_kernel<DT, R, C, WAVES, false, ODD, TAIL>;
-}
-
 template <int DT, int R, int C, int WAVES>
 hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus,
                       hipStream_t stream) {
@@ -892,17 +879,17 @@ hipError_t launch_cfg(const MatmulArgs& a, const MapBuffers& buf, int device_cus
     const uint64_t ntiles = (a.n + BN - 1) / BN;
     // every bucket adds at most one partial row tile
     const uint64_t job_bound = (routed / BM + a.n_experts + 1) * ntiles;
-    // the streamed form needs vector rows and two or more rounds (three or
-    // more when their number is odd)
+    // the streamed form needs vector rows, two or more rounds (three or more
+    // when their number is odd) and 4 weight rows within 32-bit lane offsets
     const uint32_t rounds = (a.k + kRoundK - 1) / kRoundK;
     const bool odd = rounds % 2 == 1, tail = a.k % kRoundK != 0;
-    const bool stream_form = a.vec && rounds >= (odd ? 3u : 2u);
-    const bool w32 = (uint64_t)a.n * a.k * DtypeSize<DT>::value + 256 <= 0xffffffffull;
+    const bool stream_form = a.vec && rounds >= (odd ? 3u : 2u) &&
+                             4ull * a.k * DtypeSize<DT>::value + 1024 <= 0xffffffffull;
     auto kernel = !stream_form ? grouped_kernel<DT, R, C, WAVES>
-                  : odd ? (tail ? stream_kernel<DT, R, C, WAVES, true, true>(w32)
-                                : stream_kernel<DT, R, C, WAVES, true, false>(w32))
-                        : (tail ? stream_kernel<DT, R, C, WAVES, false, true>(w32)
-                                : stream_kernel<DT, R, C, WAVES, false, false>(w32));
+                  : odd ? (tail ? grouped_stream_kernel<DT, R, C, WAVES, true, true>
+                                : grouped_stream_kernel<DT, R, C, WAVES, true, false>)
+                        : (tail ? grouped_stream_kernel<DT, R, C, WAVES, false, true>
+                                : grouped_stream_kernel<DT, R, C, WAVES, false, false>);
     const size_t table = stream_form ? (3 * (size_t)a.n_experts + 4 + 64 * BM) : (a.n_experts + 2);
     const size_t lds = (stream_form ? 4 : 2) * BM * kRoundK * sizeof(float) + table * sizeof(uint32_t);
     int per_cu = 0;
