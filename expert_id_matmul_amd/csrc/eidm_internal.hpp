@@ -84,7 +84,10 @@ bool grouped16_supported(const MatmulArgs& a);
 hipError_t launch_grouped16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 // jobs of at most this many rounds of k run the build of the same kernel
 // that keeps its accumulators in the accumulation registers
-constexpr uint32_t kG16AccRounds = 8;
+#ifndef EIDM_G16_ACC_ROUNDS
+#define EIDM_G16_ACC_ROUNDS 12
+#endif
+constexpr uint32_t kG16AccRounds = EIDM_G16_ACC_ROUNDS;
 hipError_t launch_grouped16_acc(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 // The split-16 arithmetic: the activation split (input -> a.xsplit), then
 // the Direct or the Grouped form.
