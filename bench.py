@@ -15,8 +15,10 @@ to it in TFLOP/s.
 
 A decode step is one launch of the fused kernel (route, Direct matmul and
 combine).  Exactly --steps steps are captured into one HIP graph and replayed
-once between two HIP events on the replaying stream, so the per-step time is
-that kernel's average launch duration.  The GPU clocks take a few hundred
+once between two HIP events on the replaying stream, right behind a replay
+of the warm-up graph (so the GPU is busy and at its working clocks when the
+start event is taken), so the per-step time is that kernel's average launch
+duration plus the graph's gaps and its one-time start and end.  The GPU clocks take a few hundred
 milliseconds of load to ramp up, so every measurement is preceded by at
 least --warmup steps and at least half a second of the same work; the line
 reports both what was asked and what ran.  Prefill matmul calls (id map +
@@ -96,7 +98,10 @@ def _capture(step_fn, n: int, start: int = 0) -> torch.cuda.CUDAGraph:
 
 class Timed:
     """Warm up on a graph of `warm_n` steps for at least `warmup` steps and
-    WARMUP_FLOOR_S seconds, then time one graph of exactly `steps` steps."""
+    WARMUP_FLOOR_S seconds, replay the timed graph once untimed, then time
+    one replay of that graph of exactly `steps` steps, queued right behind
+    one more replay of the warm-up graph (all untimed steps are counted in
+    warmup_steps_run)."""
 
     def __init__(self, step_fn, warm_n: int):
         self.step_fn = step_fn
@@ -116,15 +121,21 @@ class Timed:
     def run(self, steps: int, warmup: int, repeats: int = 1):
         timed = _capture(self.step_fn, steps)
         wsteps, wsecs = self.warm_up(warmup)
+        # one untimed replay of the timed graph itself: a graph's first launch
+        # also uploads it to the device, which is not part of a step
+        timed.replay()
+        torch.cuda.synchronize()
+        wsteps += steps
         times = []
         for _ in range(repeats):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            # a short GPU spin ahead of the start event keeps the GPU busy
-            # while the host submits the graph, so the interval holds the
-            # steps only
-            torch.cuda._sleep(SPIN_CYCLES)
+            # the warm-up graph runs right ahead of the start event: the GPU
+            # stays busy (and at its working clocks) while the host submits
+            # the timed graph, so the interval holds the steps only
+            self.warm.replay()
+            wsteps += self.warm_n
             start.record()
             timed.replay()
             end.record()
