@@ -559,3 +559,42 @@ def test_router_sigmoid_bits_over_ten_million_logits(lib):
     o = sigma.view(np.uint32).reshape(-1)
     bad = np.flatnonzero(g != o)
     assert bad.size == 0, f"{bad.size} sigma values differ, e.g. logit {logits.reshape(-1)[bad[:3]]}"
+
+
+# ------------------------------------------------------- uneven expert loads
+def _zipf_ids(m: int, top_k: int, n_experts: int, seed: int, a: float = 1.2) -> np.ndarray:
+    """Distinct ids per token drawn with P(e) proportional to 1/(e+1)^a: a few
+    experts with hundreds of rows, many with 1 to 48, some with none."""
+    rng = np.random.default_rng(seed)
+    p = 1.0 / np.arange(1, n_experts + 1) ** a
+    p /= p.sum()
+    return np.stack([rng.choice(n_experts, size=top_k, replace=False, p=p) for _ in range(m)]).astype(np.uint32)
+
+
+@pytest.mark.parametrize("dtype,k", [(W.DT_BF16, 384), (W.DT_F16, 1000), (W.DT_BF16, 2048)],
+                         ids=["bf16_k384", "f16_k1000", "bf16_k2048"])
+def test_uneven_expert_loads_bit_identity(lib, dtype, k):
+    """Expert row counts from a heavy-tailed draw, over 16 column tiles: the
+    Grouped kernel cuts its job list into XCD shares by cost (a job of at
+    most 16 rows costs half), so the cuts land inside buckets, between and
+    among their short last tiles.  Every output must still be computed once,
+    equal to Direct's bits and to the documented order, and within the bar of
+    the oracle (k = 384 and 1000 run the build with accumulators in the
+    accumulation registers, k = 2048 the other)."""
+    from helpers import host_threads
+    wl = _wl(f"uneven_{dtype}_{k}", dtype, 600, 1000, k, 4, 96, seed=90 + k % 7)
+    print(f"[case] uneven expert loads dtype={dtype} k={k}", flush=True)
+    wb = W.weight_bytes(wl)
+    x = W.activations(wl)
+    ids = _zipf_ids(wl.m, wl.top_k, wl.n_experts, seed=k)
+    counts = np.bincount(ids.reshape(-1), minlength=wl.n_experts)
+    assert counts.max() > 256 and ((counts > 0) & (counts % 32 <= 16) & (counts % 32 > 0)).sum() > 10
+    wdev = to_dev(wb)
+    yd = run_matmul(lib, wl, wdev, x, ids, B.DIRECT)
+    yg = run_matmul(lib, wl, wdev, x, ids, B.GROUPED)
+    assert np.array_equal(yd.view(np.uint32), yg.view(np.uint32)), "Direct and Grouped differ"
+    threads = host_threads()
+    assert np.array_equal(yd.view(np.uint32), canonical_matmul_id(wl, wb, x, ids, threads=threads).view(np.uint32))
+    ref = oracle.matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout, wb, x,
+                                   ids, threads)
+    assert_close(yd, ref, what=wl.name)
