@@ -79,3 +79,37 @@ def test_ffn_prefill_full_size_sampled_tokens(lib):
                              parts["gate"].stride, parts["down"].stride, raw["gate"], raw["up"], raw["down"],
                              xh[tokens], ids_o[tokens], gates_o[tokens])
     assert_close(out.cpu().numpy()[tokens], want, what="ffn prefill sampled tokens")
+
+
+def test_ffn_prefill_full_size_every_token(lib):
+    """The same FFN over every token against the oracle (tokens are
+    independent, so the oracle runs on chunks of tokens on the host's cores),
+    and the Direct route's output equal to the Grouped route's bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+    from helpers import host_threads
+    fw = W.FFN_WORKLOADS["ffn_prefill"]
+    print("[case] ffn prefill full size, every token", flush=True)
+    wdev = _device_weights(fw)
+    xh, lh, bh = W.ffn_inputs(fw)
+    x, logits, bias = to_dev(xh), to_dev(lh), to_dev(bh)
+    taken, ids, gates, out = _run(lib, fw, wdev, x, logits, bias, B.GROUPED)
+    assert taken == B.GROUPED
+    taken_d, ids_d, _, out_d = _run(lib, fw, wdev, x, logits, bias, B.DIRECT)
+    assert taken_d == B.DIRECT and torch.equal(ids, ids_d)
+    assert torch.equal(out.view(torch.int32), out_d.view(torch.int32)), "Direct and Grouped FFN outputs differ"
+    ids_o, gates_o, _, _ = oracle.route(lh, bh, fw.top_k)
+    assert np.array_equal(u32(ids), ids_o)
+    parts = {w: fw.part(w) for w in ("gate", "up", "down")}
+    raw = {w: t.cpu().numpy() for w, t in wdev.items()}
+    chunks = np.array_split(np.arange(fw.m), host_threads())
+
+    def run(tok):
+        want, _ = oracle.moe_ffn(fw.dtype, len(tok), fw.hidden, fw.inter, fw.top_k, fw.n_experts,
+                                 parts["gate"].stride, parts["down"].stride, raw["gate"], raw["up"], raw["down"],
+                                 xh[tok], ids_o[tok], gates_o[tok])
+        return want
+
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        want = np.concatenate(list(ex.map(run, chunks)))
+    err = assert_close(out.cpu().numpy(), want, what="ffn prefill every token")
+    print(f"[case] ffn prefill every token: max rel err {err:.3e}", flush=True)

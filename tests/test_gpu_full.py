@@ -158,6 +158,15 @@ def test_down_projection_full_path(lib):
     lib.matmul_id(shape, B.DIRECT, wdev, to_dev(x), ids, yd, weight_bytes=wl.weight_bytes)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int32), yd.view(torch.int32))
+    # every output of y, and every token of out, against the oracle (threaded)
+    from helpers import host_threads
+    wb = wdev.cpu().numpy()
+    y_all = oracle.matmul_id_threads(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout, wb,
+                                     x, ids_o, host_threads())
+    err_y = assert_close(yh, y_all, what="down_proj every output of y")
+    out_all = oracle.combine(y_all, gates_o, wl.top_k)
+    err_o = assert_close(out.cpu().numpy(), out_all, what="down_proj every token of out")
+    print(f"[case] down projection: every y max rel err {err_y:.3e}, every out {err_o:.3e}", flush=True)
 
 
 def test_graph_replays_match_eager(lib):
