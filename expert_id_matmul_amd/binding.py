@@ -33,7 +33,7 @@ EXPORTS = ["eidm_abi_version", "eidm_last_error", "eidm_query", "eidm_route_topk
 KERNELS = {1: "route", 2: "map_one_pass", 3: "map_histogram", 4: "map_scatter", 5: "direct",
            6: "grouped_16x16", 7: "grouped_stream", 8: "grouped_job", 9: "combine",
            10: "fused_decode", 11: "silu_mul", 12: "validate", 13: "proof", 14: "split_x",
-           15: "direct_split16", 16: "grouped_split16"}
+           15: "direct_split16", 16: "grouped_split16", 17: "map_split_x"}
 MAX_RECORDED_LAUNCHES = 16
 
 

@@ -303,13 +303,19 @@ int run_matmul(const eidm::MatmulArgs& args, const eidm::MapBuffers& buf, int ch
                hipStream_t stream, bool build_map = true) {
     hipError_t err;
     if (args.arith == EIDM_ARITH_SPLIT16) {
-        err = eidm::launch_split16_x(args, stream);
-        if (err != hipSuccess) return device_fail(err, "activation split launch");
-        if (chosen == EIDM_ROUTE_GROUPED) {
-            if (build_map) {
+        if (chosen == EIDM_ROUTE_GROUPED && build_map && eidm::map_split16_x_fits(args)) {
+            // the map and the activation split side by side in one launch
+            err = eidm::launch_map_split16_x(args, buf, stream);
+            if (err != hipSuccess) return device_fail(err, "map and activation split launch");
+        } else {
+            err = eidm::launch_split16_x(args, stream);
+            if (err != hipSuccess) return device_fail(err, "activation split launch");
+            if (chosen == EIDM_ROUTE_GROUPED && build_map) {
                 err = eidm::launch_map(args.ids, args.m * args.top_k, args.n_experts, buf, stream);
                 if (err != hipSuccess) return device_fail(err, "map launch");
             }
+        }
+        if (chosen == EIDM_ROUTE_GROUPED) {
             err = eidm::launch_grouped_split16(args, buf, device_cus(), stream);
             if (err != hipSuccess) return device_fail(err, "split-16 grouped launch");
         } else {

@@ -94,6 +94,10 @@ hipError_t launch_grouped16_acc(const MatmulArgs& a, const MapBuffers& buf, int 
 // bytes of the split activations of in_rows rows of k elements
 uint64_t split16_bytes(uint64_t in_rows, uint32_t k);
 hipError_t launch_split16_x(const MatmulArgs& a, hipStream_t stream);
+// the id -> row map (one-launch form) and the activation split in one launch,
+// when the map fits that form
+bool map_split16_x_fits(const MatmulArgs& a);
+hipError_t launch_map_split16_x(const MatmulArgs& a, const MapBuffers& buf, hipStream_t stream);
 hipError_t launch_direct_split16(const MatmulArgs& a, hipStream_t stream);
 hipError_t launch_grouped_split16(const MatmulArgs& a, const MapBuffers& buf, int device_cus, hipStream_t stream);
 hipError_t launch_combine(uint32_t m, uint32_t top_k, uint32_t n, const float* y,

@@ -22,15 +22,12 @@
 // block waits for another, and the map is the same stable sort.
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
+#include "map_keyed.hpp"
 
 namespace eidm {
 namespace {
 
 constexpr int kMaxMapWaves = 16;
-
-__device__ __forceinline__ uint32_t key_of(uint32_t id, uint32_t n_experts) {
-    return id < n_experts ? id : n_experts;
-}
 
 // Lanes of this wavefront whose key equals this lane's key (active lanes only).
 __device__ __forceinline__ uint64_t same_key_lanes(uint32_t key, int nbits, bool active) {
@@ -41,10 +38,6 @@ __device__ __forceinline__ uint64_t same_key_lanes(uint32_t key, int nbits, bool
         mask &= set ? ones : ~ones;
     }
     return mask;
-}
-
-__device__ __forceinline__ uint64_t lanes_below(int lane) {
-    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
 // Exclusive scan of a[0..count) in LDS by the whole block; returns the
@@ -91,9 +84,9 @@ __global__ __launch_bounds__(64 * kMaxMapWaves) void map_hist_kernel(const uint3
     const int lane = threadIdx.x & 63;
     const uint32_t r = blockIdx.x * blockDim.x + threadIdx.x;
     const bool active = r < routed_rows;
-    const uint32_t key = active ? key_of(ids[r], n_experts) : 0;
+    const uint32_t key = active ? map_key_of(ids[r], n_experts) : 0;
     const uint64_t same = same_key_lanes(key, nbits, active);
-    if (active && (same & lanes_below(lane)) == 0) atomicAdd(&cnt[key], (uint32_t)__popcll(same));
+    if (active && (same & map_lanes_below(lane)) == 0) atomicAdd(&cnt[key], (uint32_t)__popcll(same));
     __syncthreads();
     uint32_t* out = hist + (size_t)blockIdx.x * buckets;
     for (uint32_t i = threadIdx.x; i < buckets; i += blockDim.x) out[i] = cnt[i];
@@ -135,9 +128,9 @@ __global__ __launch_bounds__(64 * kMaxMapWaves) void map_scatter_kernel(
 
     const uint32_t r = blockIdx.x * blockDim.x + tid;
     const bool active = r < routed_rows;
-    const uint32_t key = active ? key_of(ids[r], n_experts) : 0;
+    const uint32_t key = active ? map_key_of(ids[r], n_experts) : 0;
     const uint64_t same = same_key_lanes(key, nbits, active);
-    const uint32_t rank = (uint32_t)__popcll(same & lanes_below(lane));
+    const uint32_t rank = (uint32_t)__popcll(same & map_lanes_below(lane));
     if (active && rank == 0) wcnt[wave * buckets + key] = (uint32_t)__popcll(same);
     __syncthreads();
     for (uint32_t b = tid; b < buckets; b += blockDim.x) {
@@ -152,73 +145,10 @@ __global__ __launch_bounds__(64 * kMaxMapWaves) void map_scatter_kernel(
     if (active) rows[base[key] + wcnt[wave * buckets + key] + rank] = r;
 }
 
-// One block per key e (1024 threads = 16 wavefronts).  Wavefront w owns the
-// contiguous rows [w*span, (w+1)*span), span a multiple of 64, in at most
-// kMapKeyedChunks chunks of 64; so (wavefront, chunk, lane) order is row
-// order and a running count per wavefront plus a prefix over the
-// wavefronts places every row.
-constexpr int kMapKeyedWaves = 16;
-constexpr int kMapKeyedChunks = 16;
-constexpr uint32_t kMapKeyedMaxRows = 64u * kMapKeyedWaves * kMapKeyedChunks;  // 16384
-
 __global__ __launch_bounds__(64 * kMapKeyedWaves) void map_keyed_kernel(
     const uint32_t* __restrict__ ids, uint32_t routed_rows, uint32_t n_experts, uint32_t span,
     uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets, uint32_t* __restrict__ rows) {
-    __shared__ uint32_t lt_s[kMapKeyedWaves], eq_s[kMapKeyedWaves];
-    const uint32_t e = blockIdx.x;  // key: an expert, or n_experts for ids naming none
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t first = (uint32_t)wave * span + (uint32_t)lane;
-    const int chunks = (int)(span >> 6);
-    // every id of this wavefront's rows first, then the two counts.  The
-    // loads are unconditional (rows past the end re-read the last id, and
-    // routed_rows >= 1: zero dimensions are rejected on the host), so all
-    // of them are in flight together; a load under a branch would be waited
-    // for before the next one is issued.
-    uint32_t raw[kMapKeyedChunks], key[kMapKeyedChunks];
-#pragma unroll
-    for (int c = 0; c < kMapKeyedChunks; ++c) raw[c] = ids[min(first + 64u * (uint32_t)c, routed_rows - 1)];
-#pragma unroll
-    for (int c = 0; c < kMapKeyedChunks; ++c) {
-        const uint32_t r = first + 64u * (uint32_t)c;
-        key[c] = c < chunks && r < routed_rows ? key_of(raw[c], n_experts) : 0xffffffffu;
-    }
-    uint32_t lt = 0, eq = 0;
-#pragma unroll
-    for (int c = 0; c < kMapKeyedChunks; ++c) {
-        lt += (uint32_t)__popcll(__ballot(key[c] < e));
-        eq += (uint32_t)__popcll(__ballot(key[c] == e));
-    }
-    if (lane == 0) {
-        lt_s[wave] = lt;
-        eq_s[wave] = eq;
-    }
-    __syncthreads();
-    uint32_t offset = 0, count = 0, before = 0;
-#pragma unroll
-    for (int w = 0; w < kMapKeyedWaves; ++w) {
-        offset += lt_s[w];
-        count += eq_s[w];
-        if (w < wave) before += eq_s[w];
-    }
-    if (threadIdx.x == 0) {
-        counts[e] = count;
-        offsets[e] = offset;
-        if (e == 0) offsets[n_experts + 1] = routed_rows;
-    }
-    uint32_t pos = offset + before;
-    const uint64_t below = lanes_below(lane);
-#pragma unroll
-    for (int c = 0; c < kMapKeyedChunks; ++c) {
-        const uint64_t m = __ballot(key[c] == e);
-        if (key[c] == e) rows[pos + (uint32_t)__popcll(m & below)] = first + 64u * (uint32_t)c;
-        pos += (uint32_t)__popcll(m);
-    }
-}
-
-// the one-launch form reads all routed_rows ids in each of n_experts+1
-// blocks: kept to small maps with at most 2^24 id reads in total
-bool map_keyed_fits(uint32_t routed_rows, uint32_t n_experts) {
-    return routed_rows <= kMapKeyedMaxRows && (uint64_t)(n_experts + 1) * routed_rows <= (1ull << 24);
+    map_keyed_block(blockIdx.x, ids, routed_rows, n_experts, span, counts, offsets, rows);
 }
 
 int key_bits(uint32_t n_experts) {
@@ -249,8 +179,7 @@ uint64_t map_hist_elements(uint64_t routed_rows, uint32_t n_experts) {
 hipError_t launch_map(const uint32_t* ids, uint32_t routed_rows, uint32_t n_experts,
                       const MapBuffers& buf, hipStream_t stream) {
     if (map_keyed_fits(routed_rows, n_experts)) {
-        const uint32_t per_wave = (routed_rows + kMapKeyedWaves - 1) / kMapKeyedWaves;
-        const uint32_t span = (per_wave + 63) / 64 * 64;  // <= 64 * kMapKeyedChunks
+        const uint32_t span = map_keyed_span(routed_rows);
         hipLaunchKernelGGL(map_keyed_kernel, dim3(n_experts + 1), dim3(64 * kMapKeyedWaves), 0, stream, ids,
                            routed_rows, n_experts, span, buf.counts, buf.offsets, buf.rows);
         return launched(EIDM_KERNEL_MAP_ONE_PASS, n_experts + 1, 64 * kMapKeyedWaves, 0);

@@ -31,6 +31,7 @@
 
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
+#include "map_keyed.hpp"
 
 namespace eidm {
 namespace {
@@ -88,17 +89,17 @@ __device__ __forceinline__ void s16_split(float v, uint32_t& p1, uint32_t& p2, u
     p3 = s16_round<DT>(r2);
 }
 
-// xs: the zero block, then rows of s16_row_chunks(k) chunks (zero past k)
+// xs: the zero block, then rows of s16_row_chunks(k) chunks (zero past k).
+// Chunks t, t + stride, ... of the whole buffer for worker t of `stride`
+// (worker 0 also writes the zero block).
 template <int DT>
-__global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, uint32_t k, uint64_t rows,
-                                                      uint16_t* __restrict__ xs) {
+__device__ __forceinline__ void split_x_chunks(const float* __restrict__ x, uint32_t k, uint64_t rows,
+                                               uint16_t* __restrict__ xs, uint64_t t, uint64_t stride) {
     const uint32_t kc = k / 8, kcp = s16_row_chunks(k);
     const uint64_t chunks = rows * kcp;
-    if (blockIdx.x == 0 && threadIdx.x < kZeroHalves / 8)
-        reinterpret_cast<s16u32x4*>(xs)[threadIdx.x] = s16u32x4{0u, 0u, 0u, 0u};
+    if (t < kZeroHalves / 8) reinterpret_cast<s16u32x4*>(xs)[t] = s16u32x4{0u, 0u, 0u, 0u};
     uint16_t* body = xs + kZeroHalves;
-    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
-         c += (uint64_t)gridDim.x * blockDim.x) {
+    for (uint64_t c = t; c < chunks; c += stride) {
         const uint64_t row = c / kcp;
         const uint32_t ch = (uint32_t)(c - row * kcp);
         s16u32x4* out = reinterpret_cast<s16u32x4*>(body + c * kSplitChunkHalves);
@@ -113,12 +114,37 @@ __global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ 
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
         uint32_t p[3][8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) s16_split<DT>(v[t], p[0][t], p[1][t], p[2][t]);
+        for (int t8 = 0; t8 < 8; ++t8) s16_split<DT>(v[t8], p[0][t8], p[1][t8], p[2][t8]);
 #pragma unroll
         for (int q = 0; q < 3; ++q)
             out[q] = s16u32x4{p[q][0] | (p[q][1] << 16), p[q][2] | (p[q][3] << 16), p[q][4] | (p[q][5] << 16),
                               p[q][6] | (p[q][7] << 16)};
     }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void split_x_kernel(const float* __restrict__ x, uint32_t k, uint64_t rows,
+                                                      uint16_t* __restrict__ xs) {
+    split_x_chunks<DT>(x, k, rows, xs, (uint64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                       (uint64_t)gridDim.x * blockDim.x);
+}
+
+// The Grouped route's two preparations in one launch, side by side: blocks
+// 0 .. n_experts build the id -> row map (the one-launch form, block e for
+// key e), the blocks after them split the activations.  Neither reads what
+// the other writes.
+template <int DT>
+__global__ __launch_bounds__(64 * kMapKeyedWaves) void map_split_x_kernel(
+    const uint32_t* __restrict__ ids, uint32_t routed_rows, uint32_t n_experts, uint32_t span,
+    uint32_t* __restrict__ counts, uint32_t* __restrict__ offsets, uint32_t* __restrict__ rows,
+    const float* __restrict__ x, uint32_t k, uint64_t in_rows, uint16_t* __restrict__ xs) {
+    const uint32_t map_blocks = n_experts + 1;
+    if (blockIdx.x < map_blocks) {
+        map_keyed_block(blockIdx.x, ids, routed_rows, n_experts, span, counts, offsets, rows);
+        return;
+    }
+    split_x_chunks<DT>(x, k, in_rows, xs, (uint64_t)(blockIdx.x - map_blocks) * blockDim.x + threadIdx.x,
+                       (uint64_t)(gridDim.x - map_blocks) * blockDim.x);
 }
 
 // A buffer offset past every extent: a buffer load there returns zeros.
@@ -508,6 +534,27 @@ __global__ __launch_bounds__(kGs16Threads, 1) void grouped_split16_kernel(Matmul
 
 uint64_t split16_bytes(uint64_t in_rows, uint32_t k) {
     return (uint64_t)kZeroHalves * 2 + in_rows * s16_row_chunks(k) * kSplitChunkHalves * 2;
+}
+
+bool map_split16_x_fits(const MatmulArgs& a) { return map_keyed_fits(a.m * a.top_k, a.n_experts); }
+
+hipError_t launch_map_split16_x(const MatmulArgs& a, const MapBuffers& buf, hipStream_t stream) {
+    const uint32_t routed = a.m * a.top_k;
+    const uint64_t in_rows = a.layout == 1 ? (uint64_t)routed : a.m;
+    const uint64_t chunks = in_rows * s16_row_chunks(a.k);
+    constexpr uint32_t threads = 64 * kMapKeyedWaves;
+    uint64_t split_blocks = (chunks + threads - 1) / threads;
+    if (split_blocks > 4096) split_blocks = 4096;
+    if (split_blocks == 0) split_blocks = 1;
+    const uint32_t grid = a.n_experts + 1 + (uint32_t)split_blocks;
+    const uint32_t span = map_keyed_span(routed);
+    if (a.dtype == kDtypeF16)
+        hipLaunchKernelGGL(map_split_x_kernel<kDtypeF16>, dim3(grid), dim3(threads), 0, stream, a.ids, routed,
+                           a.n_experts, span, buf.counts, buf.offsets, buf.rows, a.input, a.k, in_rows, a.xsplit);
+    else
+        hipLaunchKernelGGL(map_split_x_kernel<kDtypeBF16>, dim3(grid), dim3(threads), 0, stream, a.ids, routed,
+                           a.n_experts, span, buf.counts, buf.offsets, buf.rows, a.input, a.k, in_rows, a.xsplit);
+    return launched(EIDM_KERNEL_MAP_SPLIT_X, grid, threads, 0);
 }
 
 hipError_t launch_split16_x(const MatmulArgs& a, hipStream_t stream) {

@@ -160,7 +160,9 @@ typedef enum eidm_kernel {
     EIDM_KERNEL_PROOF = 13,         /* calibration proof check                       */
     EIDM_KERNEL_SPLIT_X = 14,       /* split-16: activations into three parts        */
     EIDM_KERNEL_DIRECT_SPLIT16 = 15,  /* split-16 Direct                             */
-    EIDM_KERNEL_GROUPED_SPLIT16 = 16  /* split-16 Grouped                            */
+    EIDM_KERNEL_GROUPED_SPLIT16 = 16, /* split-16 Grouped                            */
+    EIDM_KERNEL_MAP_SPLIT_X = 17      /* split-16 Grouped: the one-launch map and the
+                                         activation split in one launch              */
 } eidm_kernel;
 
 /* One kernel launch: which kernel and its launch geometry (1-D grid of
@@ -192,7 +194,10 @@ typedef struct eidm_dispatch {
  * library entry point makes internally add to the caller's).  A successful
  * eidm_matmul_id is 1 launch for Direct; for Grouped the map (1 or 2
  * launches) and the Grouped kernel, or the Grouped kernel alone when the
- * map is reused (the later projections of eidm_moe_ffn).  An
+ * map is reused (the later projections of eidm_moe_ffn).  In the split-16
+ * arithmetic the activation split comes first (Direct: 2 launches); for
+ * Grouped it shares one launch with the map when the map takes its
+ * one-launch form (then 2 launches, else split, map, Grouped).  An
  * eidm_moe_forward that runs Direct with top_k <= 16 is 1 fused launch.
  * Enqueues nothing.
  */

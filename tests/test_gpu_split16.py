@@ -133,12 +133,32 @@ def test_split16_receipts(lib):
     w, x, ids = to_dev(W.weight_bytes(wl)), to_dev(W.activations(wl)), ids_to_dev(W.ids(wl))
     y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
     for route, kernels in ((B.DIRECT, ["split_x", "direct_split16"]),
-                           (B.GROUPED, ["split_x", "map_one_pass", "grouped_split16"])):
+                           (B.GROUPED, ["map_split_x", "grouped_split16"])):
         scratch = torch.empty(lib.query(shape, route).scratch_bytes, dtype=torch.uint8, device="cuda")
         lib.matmul_id(shape, route, w, x, ids, y, scratch)
         d = lib.last_dispatch()
         assert d.route == route and d.kernels() == kernels
     torch.cuda.synchronize()
+
+
+def test_split16_map_too_large_for_one_launch(lib):
+    """16,800 routed rows (above the one-launch map's 16,384): the split, the
+    two-launch map and the Grouped kernel run separately, with the same bits
+    as Direct."""
+    wl = _wl("s16_big_map", W.DT_BF16, 4200, 64, 256, 4, 16, seed=215)
+    print("[case] split16 two-launch map", flush=True)
+    wb = W.weight_bytes(wl)
+    xh = W.activations(wl)
+    ih = W.ids(wl)
+    w, x, ids = to_dev(wb), to_dev(xh), ids_to_dev(ih)
+    yd = _run(lib, wl, B.DIRECT, w, x, ids)
+    yg = _run(lib, wl, B.GROUPED, w, x, ids)
+    assert lib.last_dispatch().kernels() == ["split_x", "map_histogram", "map_scatter", "grouped_split16"]
+    n_out = wl.routed_rows * wl.n
+    vd, vg = check_guarded(yd, n_out), check_guarded(yg, n_out)
+    assert np.array_equal(vd.view(np.uint32), vg.view(np.uint32))
+    ref = oracle.matmul_id(wl.dtype, wl.m, wl.n, wl.k, wl.top_k, wl.n_experts, wl.stride, wl.layout, wb, xh, ih)
+    assert_close(vd.reshape(wl.routed_rows, wl.n), ref, what=wl.name)
 
 
 # ------------------------------------------------------------- full sizes
