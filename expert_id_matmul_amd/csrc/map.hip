@@ -19,7 +19,8 @@
 // block bounded) take one launch instead: block e reads every id and
 // counts the rows with key < e (its offset) and key == e (its count) with
 // two ballots per 64 ids, then writes its own rows in ascending order.  No
-// block waits for another, and the map is the same stable sort.
+// block waits for another, and the map is the same stable sort (the block
+// body is in map_keyed.hpp).
 #include "eidm_device.hpp"
 #include "eidm_internal.hpp"
 #include "map_keyed.hpp"
