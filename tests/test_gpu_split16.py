@@ -228,3 +228,41 @@ def test_split16_full_size(lib, name):
         print(f"[case] split16 full {name} every output max rel err {err:.3e}", flush=True)
     del w, ys
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("route", [B.GROUPED, B.DIRECT])
+def test_split16_graph_replays_match_eager(lib, route):
+    """A captured split-16 call (Grouped: the map-and-split launch and the
+    Grouped kernel; Direct: split and Direct) replays to the eager bits, with
+    eager calls and synchronisations between the replays."""
+    wl = _wl("s16_graph", W.DT_BF16, 96, 256, 512, 4, 8, seed=216)
+    print(f"[case] split16 graph route {route}", flush=True)
+    shape = B.shape_of(wl)
+    w, x, ids = to_dev(W.weight_bytes(wl)), to_dev(W.activations(wl)), ids_to_dev(W.ids(wl))
+    scratch = torch.empty(lib.query(shape, route).scratch_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((wl.routed_rows, wl.n), dtype=torch.float32, device="cuda")
+
+    def step():
+        lib.matmul_id(shape, route, w, x, ids, y, scratch, weight_bytes=wl.weight_bytes)
+
+    step()
+    torch.cuda.synchronize()
+    eager = y.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        y.zero_()
+        scratch.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
+        step()
+        torch.cuda.synchronize()
