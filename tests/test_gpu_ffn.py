@@ -113,3 +113,46 @@ def test_ffn_prefill_full_size_every_token(lib):
         want = np.concatenate(list(ex.map(run, chunks)))
     err = assert_close(out.cpu().numpy(), want, what="ffn prefill every token")
     print(f"[case] ffn prefill every token: max rel err {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("fw", [SMALL[3], SMALL[4]], ids=lambda f: f.name)
+def test_ffn_graph_replays_match_eager(lib, fw):
+    """A captured expert-FFN step (route, one shared map, three Grouped
+    projections, SiLU·up, combine) replays to the eager bits, with eager
+    steps and synchronisations between the replays (the 4x4x1 streamed
+    kernel at k = 256, the 16x16x1 kernel at k = 2880 and 1408)."""
+    print(f"[case] ffn graph {fw.name}", flush=True)
+    wdev = _device_weights(fw)
+    xh, lh, bh = W.ffn_inputs(fw)
+    x, logits, bias = to_dev(xh), to_dev(lh), to_dev(bh)
+    shape = B.ffn_shape_of(fw)
+    ids = torch.empty((fw.m, fw.top_k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((fw.m, fw.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((fw.m, fw.hidden), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(lib.moe_ffn_scratch_bytes(shape), dtype=torch.uint8, device="cuda")
+
+    def step():
+        lib.moe_ffn(shape, B.GROUPED, wdev["gate"], wdev["up"], wdev["down"], x, logits, bias, ids, gates, out,
+                    scratch)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.zero_()
+        scratch.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
+        step()
+        torch.cuda.synchronize()
