@@ -100,6 +100,25 @@ __device__ __forceinline__ void xstage_store(float* xs, int k, const XStage& st)
         if (i < passes) reinterpret_cast<f32x4*>(xs)[xstage_piece(i, n4)] = st.v[i];
 }
 
+// The same copy by `count` of the block's threads (this one is number
+// `idx` among them): piece i * count + idx, clamped to the last piece;
+// direct_xstage_fits(k, count) must hold.
+__device__ __forceinline__ void xstage_issue_by(const float* xrow, int k, int idx, int count, XStage& st) {
+    const int n4 = k >> 2;
+    const int passes = (n4 + count - 1) / count;
+#pragma unroll
+    for (int i = 0; i < kXStageVec; ++i)
+        if (i < passes) st.v[i] = reinterpret_cast<const f32x4*>(xrow)[min(i * count + idx, n4 - 1)];
+}
+
+__device__ __forceinline__ void xstage_store_by(float* xs, int k, int idx, int count, const XStage& st) {
+    const int n4 = k >> 2;
+    const int passes = (n4 + count - 1) / count;
+#pragma unroll
+    for (int i = 0; i < kXStageVec; ++i)
+        if (i < passes) reinterpret_cast<f32x4*>(xs)[min(i * count + idx, n4 - 1)] = st.v[i];
+}
+
 // Where direct_columns finds the activation row.
 enum : int {
     kXFromMemory = 0,  // each slot loads its slice's granule

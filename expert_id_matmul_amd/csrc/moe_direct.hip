@@ -37,7 +37,8 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
                                                                 const float* __restrict__ bias, int renormalize,
                                                                 uint32_t* __restrict__ ids,
                                                                 float* __restrict__ gates,
-                                                                float* __restrict__ out, int cols_per_block) {
+                                                                float* __restrict__ out, int cols_per_block,
+                                                                int split_roles) {
     __shared__ float ys[MAXW][4 * C];
     __shared__ float gate_s[MAXW];
     __shared__ float rs_s[64 * NV];        // the token's router entries
@@ -53,15 +54,46 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     const int col0 = (int)(blockIdx.x % col_blocks) * cols_per_block;
     const int col_end = min(col0 + cols_per_block, n);
 
-    // the activation copy goes out first and lands in LDS with the router
-    // entries, which the block computes once, under one barrier
+    // The router entries (computed once per block) and the activation row
+    // land in LDS under one barrier.  A thread's loads complete in order, so
+    // the sigmoids must not queue behind the activation copy:
+    //   * split_roles (the block has at least twice as many threads as
+    //     router entries): the first 64*NV threads score one expert each and
+    //     the others copy the activation row, so each waits for its own
+    //     loads only;
+    //   * otherwise every thread requests its router inputs first and its
+    //     share of the copy after them, and the row arrives while the
+    //     sigmoids are computed.
+    const float* lrow = logits + (size_t)t * a.n_experts;
     XStage xst;
-    if constexpr (XS) {
-        xstage_issue(a.input + (size_t)t * a.k, (int)a.k, xst);
-        __builtin_amdgcn_sched_barrier(0);
+    if (split_roles) {
+        constexpr int NE = 64 * NV;
+        const int tid = (int)threadIdx.x;
+        if (tid < NE) {  // whole wavefronts
+            const uint32_t ee = min((uint32_t)tid, a.n_experts - 1);
+            const float lg = lrow[ee];
+            const float bs = bias ? bias[ee] : 0.0f;
+            float sv = 0.0f;
+            uint32_t code = 0;
+            if ((uint32_t)tid < a.n_experts) route_entry(lg, bs, sv, code);
+            rs_s[tid] = sv;
+            rs_code[tid] = code;
+        } else if constexpr (XS) {
+            const int count = (int)blockDim.x - NE;
+            xstage_issue_by(a.input + (size_t)t * a.k, (int)a.k, tid - NE, count, xst);
+            xstage_store_by(xs, (int)a.k, tid - NE, count, xst);
+        }
+    } else {
+        RouteInputs<NV> rin;
+        route_inputs_issue<NV>(lrow, bias, a.n_experts, rin);
+        if constexpr (XS) {
+            __builtin_amdgcn_sched_barrier(0);
+            xstage_issue(a.input + (size_t)t * a.k, (int)a.k, xst);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        route_inputs_score<NV>(rin, a.n_experts, rs_s, rs_code);
+        if constexpr (XS) xstage_store(xs, (int)a.k, xst);
     }
-    route_scores_shared<NV>(logits + (size_t)t * a.n_experts, bias, a.n_experts, rs_s, rs_code);
-    if constexpr (XS) xstage_store(xs, (int)a.k, xst);
     __syncthreads();
 
     // every wavefront runs the selection up to its own pick; the last one
@@ -139,15 +171,18 @@ hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bia
     const dim3 grid(col_blocks * a.m);
     constexpr int D = moe_depth<DT, MAXW>();
     // with one activation row per token, the block's wavefronts share it
-    // through LDS when they can stage it in one pass
-    const bool xs = a.layout == 0 && a.vec && direct_xstage_fits(a.k, 64 * a.top_k);
+    // through LDS when they can stage it in one pass (by the threads that
+    // score no expert, when there are at least as many of those)
+    const uint32_t threads = 64 * a.top_k;
+    const int split = threads >= 2u * 64 * NV ? 1 : 0;
+    const bool xs = a.layout == 0 && a.vec && direct_xstage_fits(a.k, split ? threads - 64 * NV : threads);
     if (xs)
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true>), grid, dim3(64 * a.top_k),
-                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb);
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true>), grid, dim3(threads), (size_t)a.k * 4,
+                           stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
     else
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false>), grid, dim3(64 * a.top_k), 0,
-                           stream, a, logits, bias, renormalize, ids, gates, out, cb);
-    return launched(EIDM_KERNEL_FUSED_DECODE, grid.x, 64 * a.top_k, xs ? a.k * 4 : 0);
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false>), grid, dim3(threads), 0, stream, a,
+                           logits, bias, renormalize, ids, gates, out, cb, split);
+    return launched(EIDM_KERNEL_FUSED_DECODE, grid.x, threads, xs ? a.k * 4 : 0);
 }
 
 template <int DT>

@@ -92,30 +92,52 @@ __device__ __forceinline__ void route_scores(const float* __restrict__ lrow, con
 // its copy with route_scores_lds.  The double-precision sigmoid is the
 // router's costliest step, so a block of W wavefronts spreads it W ways
 // instead of repeating it in every wavefront.
+// The block's share of one token's router inputs, requested but not yet
+// waited for: thread i holds experts i, i + blockDim.x, ... (64*NV slots).
 template <int NV>
-__device__ __forceinline__ void route_scores_shared(const float* __restrict__ lrow, const float* __restrict__ bias,
-                                                    uint32_t n_experts, float* s_lds, uint32_t* code_lds) {
-    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
+struct RouteInputs {
     float lg[NV], bs[NV];
+};
+
+template <int NV>
+__device__ __forceinline__ void route_inputs_issue(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                                   uint32_t n_experts, RouteInputs<NV>& in) {
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         if (i * nt < 64 * NV) {  // block-uniform
             const uint32_t e = min((uint32_t)(i * nt + tid), n_experts - 1);
-            lg[i] = lrow[e];
-            bs[i] = bias ? bias[e] : 0.0f;
+            in.lg[i] = lrow[e];
+            in.bs[i] = bias ? bias[e] : 0.0f;
         }
     }
+}
+
+// The sigmoids and rank codes of the inputs into LDS (s_lds, code_lds: 64*NV
+// entries, those past n_experts as 0).
+template <int NV>
+__device__ __forceinline__ void route_inputs_score(const RouteInputs<NV>& in, uint32_t n_experts, float* s_lds,
+                                                   uint32_t* code_lds) {
+    const int tid = (int)threadIdx.x, nt = (int)blockDim.x;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = i * nt + tid;
         if (i * nt < 64 * NV && e < 64 * NV) {
             float s = 0.0f;
             uint32_t code = 0;
-            if ((uint32_t)e < n_experts) route_entry(lg[i], bs[i], s, code);
+            if ((uint32_t)e < n_experts) route_entry(in.lg[i], in.bs[i], s, code);
             s_lds[e] = s;
             code_lds[e] = code;
         }
     }
+}
+
+template <int NV>
+__device__ __forceinline__ void route_scores_shared(const float* __restrict__ lrow, const float* __restrict__ bias,
+                                                    uint32_t n_experts, float* s_lds, uint32_t* code_lds) {
+    RouteInputs<NV> in;
+    route_inputs_issue<NV>(lrow, bias, n_experts, in);
+    route_inputs_score<NV>(in, n_experts, s_lds, code_lds);
 }
 
 template <int NV>
