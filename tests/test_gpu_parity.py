@@ -383,8 +383,12 @@ def test_moe_forward_small_down_projection(lib, route):
     (W.DT_BF16, 5, 48, 384, 1, 7, W.LAYOUT_SLOTTED),       # one slot
     (W.DT_BF16, 2, 96, 512, 8, 1000, W.LAYOUT_SHARED),     # > 256 experts, staged activation row
     (W.DT_BF16, 1, 24, 8320, 2, 16, W.LAYOUT_SHARED),      # row too long to stage: read from memory
+    # 8 slots and at most 256 experts: the first 256 threads score the experts
+    # (those past n_experts as empty entries) while the others copy the row
+    (W.DT_F16, 1, 300, 2048, 8, 130, W.LAYOUT_SHARED),
+    (W.DT_BF16, 2, 100, 512, 8, 200, W.LAYOUT_SLOTTED),    # the same split with no row to copy
 ], ids=["bf16_decode_like", "f32_many_experts", "f16_top16", "bf16_top1", "bf16_many_experts_shared",
-        "bf16_long_k_shared"])
+        "bf16_long_k_shared", "f16_split_roles_130_experts", "bf16_split_roles_slotted"])
 def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k, top_k, n_experts, layout):
     """With the Direct route the whole path runs as one kernel; its ids, gates,
     y and out must be the bits of route_topk -> matmul_id -> combine."""
