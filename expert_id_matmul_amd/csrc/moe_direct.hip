@@ -43,6 +43,7 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     __shared__ float gate_s[MAXW];
     __shared__ float rs_s[64 * NV];        // the token's router entries
     __shared__ uint32_t rs_code[64 * NV];
+    __shared__ uint32_t first_code[NV], first_idx[NV];  // each scoring wavefront's best entry
     extern __shared__ __align__(16) float xs[];  // token t's activation row (XS)
     const int lane = threadIdx.x & 63;
     const int slot = threadIdx.x >> 6;
@@ -78,6 +79,14 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
             if ((uint32_t)tid < a.n_experts) route_entry(lg, bs, sv, code);
             rs_s[tid] = sv;
             rs_code[tid] = code;
+            // this wavefront's best entry (the highest code, the lowest
+            // expert index among equals), for the first pick
+            const uint32_t best = wave_max_u32(code);
+            const uint64_t hit = __ballot(code == best);
+            if ((tid & 63) == 0) {
+                first_code[tid >> 6] = best;
+                first_idx[tid >> 6] = (uint32_t)(tid & ~63) + (uint32_t)__builtin_ctzll(hit);
+            }
         } else if constexpr (XS) {
             const int count = (int)blockDim.x - NE;
             xstage_issue_by(a.input + (size_t)t * a.k, (int)a.k, tid - NE, count, xst);
@@ -97,23 +106,40 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     __syncthreads();
 
     // every wavefront runs the selection up to its own pick; the last one
-    // runs all top_k picks and forms the gates
-    RouteScores<NV> sc;
-    route_scores_lds<NV>(rs_s, rs_code, sc);
-    uint32_t pick;
-    float score;
-    const float sum = route_select<NV>(sc, (uint32_t)slot + 1, pick, score);
-    if (slot == (int)top_k - 1) {
-        const float gate = renormalize ? __fdiv_rn(score, sum) : score;
-        if (lane < (int)top_k) {
-            gate_s[lane] = gate;
-            if (col0 == 0) {
-                ids[(size_t)t * top_k + lane] = pick;
-                gates[(size_t)t * top_k + lane] = gate;
+    // runs all top_k picks and forms the gates.  With split roles the first
+    // pick is the best of the scoring wavefronts' best entries (the first
+    // wavefront, lowest expert indices, wins among equal codes), so the
+    // first slot's wavefront starts streaming without scanning the entries.
+    uint32_t e;
+    if (split_roles && slot == 0 && top_k > 1) {
+        uint32_t bc = first_code[0], bi = first_idx[0];
+#pragma unroll
+        for (int w = 1; w < NV; ++w) {
+            const uint32_t c = first_code[w];
+            if (c > bc) {
+                bc = c;
+                bi = first_idx[w];
             }
         }
+        e = bi;
+    } else {
+        RouteScores<NV> sc;
+        route_scores_lds<NV>(rs_s, rs_code, sc);
+        uint32_t pick;
+        float score;
+        const float sum = route_select<NV>(sc, (uint32_t)slot + 1, pick, score);
+        if (slot == (int)top_k - 1) {
+            const float gate = renormalize ? __fdiv_rn(score, sum) : score;
+            if (lane < (int)top_k) {
+                gate_s[lane] = gate;
+                if (col0 == 0) {
+                    ids[(size_t)t * top_k + lane] = pick;
+                    gates[(size_t)t * top_k + lane] = gate;
+                }
+            }
+        }
+        e = (uint32_t)__builtin_amdgcn_readlane((int)pick, slot);
     }
-    const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)pick, slot);
     const uint32_t r = t * top_k + (uint32_t)slot;
 
     float v[C];
