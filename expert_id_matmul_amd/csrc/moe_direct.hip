@@ -7,7 +7,11 @@
 //     into LDS); every wavefront then runs the router's selection
 //     (route_wave.hpp, the router kernel's own code) up to pick s, its
 //     expert; the last wavefront runs all top_k picks and forms the gates,
-//     so picks and gates are bit for bit the router kernel's;
+//     so picks and gates are bit for bit the router kernel's (with split
+//     roles the first slot takes the best of the scoring wavefronts' best
+//     entries, which is the selection's first pick);
+//   * the wavefronts start their weight streams one pick (about 0.2 us)
+//     apart, which measured faster than starting them together;
 //   * it computes its routed row t*top_k+s over the block's columns exactly
 //     as the Direct kernel does (direct_columns), and stores y;
 //   * the top_k rows of the block's columns meet in LDS and one wavefront
