@@ -146,8 +146,9 @@ __device__ __forceinline__ void xstage_only(int k, float* xs, const XStage& st) 
 // blockDim.x), and xs is LDS for its k floats.  With kXStageInRing every
 // wavefront of the block has issued the copy (xstage_issue into *xst) and
 // then calls this (or xstage_only): issuing the copy early lets its latency
-// hide under the ring's fill.
-template <int DT, int C, int D, bool NT, int XM>
+// hide under the ring's fill.  WHOLE: the caller guarantees 16-byte rows and
+// k a multiple of 128, so every round takes the pipelined path.
+template <int DT, int C, int D, bool NT, int XM, bool WHOLE = false>
 __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, uint32_t e, int col0,
                                                int col_end, float (&v)[C], bool (&cvalid)[C],
                                                float* xs, const XStage* xst) {
@@ -173,7 +174,7 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
 
     const int rounds = (k + kRoundK - 1) / kRoundK;
     // rounds whose granules are whole and 16-byte aligned: the pipelined path
-    const int full = a.vec ? k / kRoundK : 0;
+    const int full = (WHOLE || a.vec) ? k / kRoundK : 0;
 
     auto fetch = [&](int g, DirectSlot<DT, C>& s) {
 #pragma unroll
@@ -258,7 +259,7 @@ __device__ __forceinline__ void direct_columns(const MatmulArgs& a, uint32_t r, 
         __syncthreads();
     }
     // rounds that need masked loads (k tail, or rows not 16-byte aligned)
-    for (int g = full; g < rounds; ++g) {
+    for (int g = full; !WHOLE && g < rounds; ++g) {
         float x[kGranule];
         load_input_granule(xrow, g * kRoundK + b * kGranule, k, true, false, x);
         float w[C][kGranule];

@@ -36,7 +36,7 @@
 namespace eidm {
 namespace {
 
-template <int DT, int C, int D, int NV, int MAXW, bool XS>
+template <int DT, int C, int D, int NV, int MAXW, bool XS, bool WHOLE>
 __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, const float* __restrict__ logits,
                                                                 const float* __restrict__ bias, int renormalize,
                                                                 uint32_t* __restrict__ ids,
@@ -148,7 +148,8 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
 
     float v[C];
     bool cvalid[C];
-    direct_columns<DT, C, D, true, XS ? kXInLds : kXFromMemory>(a, r, e, col0, col_end, v, cvalid, xs, nullptr);
+    direct_columns<DT, C, D, true, XS ? kXInLds : kXFromMemory, WHOLE>(a, r, e, col0, col_end, v, cvalid, xs,
+                                                                         nullptr);
     if (b == 0) {
         float* yrow = a.output + (size_t)r * a.n;
 #pragma unroll
@@ -206,12 +207,18 @@ hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bia
     const uint32_t threads = 64 * a.top_k;
     const int split = threads >= 2u * 64 * NV ? 1 : 0;
     const bool xs = a.layout == 0 && a.vec && direct_xstage_fits(a.k, split ? threads - 64 * NV : threads);
-    if (xs)
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true>), grid, dim3(threads), (size_t)a.k * 4,
-                           stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
+    // whole 128-element rounds (decode's k = 4096): a build without the
+    // masked tail rounds
+    const bool whole = xs && a.k % kRoundK == 0;
+    if (whole)
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true, true>), grid, dim3(threads),
+                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
+    else if (xs)
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true, false>), grid, dim3(threads),
+                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
     else
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false>), grid, dim3(threads), 0, stream, a,
-                           logits, bias, renormalize, ids, gates, out, cb, split);
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false, false>), grid, dim3(threads), 0, stream,
+                           a, logits, bias, renormalize, ids, gates, out, cb, split);
     return launched(EIDM_KERNEL_FUSED_DECODE, grid.x, threads, xs ? a.k * 4 : 0);
 }
 
