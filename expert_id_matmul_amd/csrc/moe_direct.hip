@@ -23,6 +23,8 @@
 //
 // cortiq-engine 0.7.7, src/mimo_moe.rs, Dynamic::run: routing, one expert
 // product per pick, and the weighted sum of the picks, per token.
+#include <type_traits>
+
 #include "direct_wave.hpp"
 #include "route_wave.hpp"
 
@@ -36,13 +38,13 @@
 namespace eidm {
 namespace {
 
-template <int DT, int C, int D, int NV, int MAXW, bool XS, bool WHOLE>
+template <int DT, int C, int D, int NV, int MAXW, bool XS, bool WHOLE, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, const float* __restrict__ logits,
                                                                 const float* __restrict__ bias, int renormalize,
                                                                 uint32_t* __restrict__ ids,
                                                                 float* __restrict__ gates,
-                                                                float* __restrict__ out, int cols_per_block,
-                                                                int split_roles) {
+                                                                float* __restrict__ out, int cols_per_block) {
+    constexpr bool split_roles = SPLIT;
     __shared__ float ys[MAXW][4 * C];
     __shared__ float gate_s[MAXW];
     __shared__ float rs_s[64 * NV];        // the token's router entries
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(64 * MAXW) void moe_direct_kernel(MatmulArgs a, con
     //     sigmoids are computed.
     const float* lrow = logits + (size_t)t * a.n_experts;
     XStage xst;
-    if (split_roles) {
+    if constexpr (SPLIT) {
         constexpr int NE = 64 * NV;
         const int tid = (int)threadIdx.x;
         if (tid < NE) {  // whole wavefronts
@@ -210,15 +212,22 @@ hipError_t launch_cfg(const MatmulArgs& a, const float* logits, const float* bia
     // whole 128-element rounds (decode's k = 4096): a build without the
     // masked tail rounds
     const bool whole = xs && a.k % kRoundK == 0;
-    if (whole)
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true, true>), grid, dim3(threads),
-                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
-    else if (xs)
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, true, false>), grid, dim3(threads),
-                           (size_t)a.k * 4, stream, a, logits, bias, renormalize, ids, gates, out, cb, split);
-    else
-        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, false, false>), grid, dim3(threads), 0, stream,
-                           a, logits, bias, renormalize, ids, gates, out, cb, split);
+    auto go = [&](auto xsc, auto wholec, auto splitc) {
+        constexpr bool X = decltype(xsc)::value, WH = decltype(wholec)::value, SP = decltype(splitc)::value;
+        hipLaunchKernelGGL((moe_direct_kernel<DT, C, D, NV, MAXW, X, WH, SP>), grid, dim3(threads),
+                           X ? (size_t)a.k * 4 : 0, stream, a, logits, bias, renormalize, ids, gates, out, cb);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    if (split) {
+        if (whole) go(T{}, T{}, T{});
+        else if (xs) go(T{}, F{}, T{});
+        else go(F{}, F{}, T{});
+    } else {
+        if (whole) go(T{}, T{}, F{});
+        else if (xs) go(T{}, F{}, F{});
+        else go(F{}, F{}, F{});
+    }
     return launched(EIDM_KERNEL_FUSED_DECODE, grid.x, threads, xs ? a.k * 4 : 0);
 }
 
