@@ -387,8 +387,12 @@ def test_moe_forward_small_down_projection(lib, route):
     # (those past n_experts as empty entries) while the others copy the row
     (W.DT_F16, 1, 300, 2048, 8, 130, W.LAYOUT_SHARED),
     (W.DT_BF16, 2, 100, 512, 8, 200, W.LAYOUT_SLOTTED),    # the same split with no row to copy
+    # staged row with a partial last round and too many experts to split
+    # the roles (512 threads, 320 router entries)
+    (W.DT_F16, 2, 70, 1000, 8, 300, W.LAYOUT_SHARED),
 ], ids=["bf16_decode_like", "f32_many_experts", "f16_top16", "bf16_top1", "bf16_many_experts_shared",
-        "bf16_long_k_shared", "f16_split_roles_130_experts", "bf16_split_roles_slotted"])
+        "bf16_long_k_shared", "f16_split_roles_130_experts", "bf16_split_roles_slotted",
+        "f16_staged_tail_shared_roles"])
 def test_moe_forward_direct_matches_the_three_calls_bitwise(lib, dtype, m, n, k, top_k, n_experts, layout):
     """With the Direct route the whole path runs as one kernel; its ids, gates,
     y and out must be the bits of route_topk -> matmul_id -> combine."""
